@@ -1,0 +1,176 @@
+"""CPU oracle for D = A*B + C -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library never imports it and shares no code with it; the
+only thing both sides consume is the seeded input generator in ``synth``.
+
+The arithmetic lives in ``oracle_gemm.c`` (a plain fp64/int64 triple loop that
+evaluates the definition D = x(C) + sum_k x(A) x(B) with exact decoding x of
+every stored element; pages: "CDNA2 dense MFMA builtins", section "Naming
+convention" -- the product is the sum over all K panels of the per-step
+contributions -- and "RDNA3 dense WMMA builtins", builtin reference, where a
+step returns srcA x srcB + srcC).  This module only marshals numpy arrays into
+it, and states the float tolerance the GPU result is held to.
+
+Storage conventions (shared with the GPU library's ABI, restated here):
+  * fp16 / bf16 inputs are passed as uint16 bit patterns, fp32 C as float32,
+    int8 inputs as int8 and int32 C as int32;
+  * A row-major: A[i, k] = A_mem[i*lda + k];  col-major: A_mem[i + k*lda];
+  * B row-major: B[k, j] = B_mem[k*ldb + j];  col-major: B_mem[k + j*ldb];
+  * C row-major with ldc;  batch b is offset by a stride per operand.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle_gemm.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"f16": 0, "bf16": 1, "i8": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with the host C compiler (always rebuilds)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64 = ctypes.c_int64
+    vp = ctypes.c_void_p
+    lib.oracle_decode_f16.restype = ctypes.c_double
+    lib.oracle_decode_f16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_bf16.restype = ctypes.c_double
+    lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_f32.restype = ctypes.c_double
+    lib.oracle_decode_f32.argtypes = [ctypes.c_uint32]
+    lib.oracle_gemm_float.restype = ctypes.c_int
+    lib.oracle_gemm_float.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp,
+                                      i64, i64, i64, i64, i64, i64,
+                                      ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_int8.restype = ctypes.c_int
+    lib.oracle_gemm_int8.argtypes = [vp, vp, vp, vp,
+                                     i64, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_points.restype = ctypes.c_int
+    lib.oracle_gemm_points.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp,
+                                       i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_int, ctypes.c_int, i64, i64, i64, i64]
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check_storage(dtype: str, A, B, C):
+    if dtype in ("f16", "bf16"):
+        assert A.dtype == np.uint16 and B.dtype == np.uint16, "16-bit inputs are uint16 bit patterns"
+        assert C.dtype == np.float32
+    elif dtype == "i8":
+        assert A.dtype == np.int8 and B.dtype == np.int8 and C.dtype == np.int32
+    else:
+        raise ValueError(dtype)
+    for x in (A, B, C):
+        assert x.flags["C_CONTIGUOUS"]
+
+
+def decode(dtype: str, bits: np.ndarray) -> np.ndarray:
+    """Exact decode of fp16 / bf16 bit patterns (uint16) to float64, element by element."""
+    lib = _load()
+    fn = lib.oracle_decode_f16 if dtype == "f16" else lib.oracle_decode_bf16
+    flat = np.asarray(bits, dtype=np.uint16).ravel()
+    out = np.empty(flat.shape, dtype=np.float64)
+    for n, h in enumerate(flat.tolist()):
+        out[n] = fn(h)
+    return out.reshape(np.shape(bits))
+
+
+def decode_f32(words: np.ndarray) -> np.ndarray:
+    lib = _load()
+    flat = np.asarray(words, dtype=np.uint32).ravel()
+    out = np.array([lib.oracle_decode_f32(w) for w in flat.tolist()], dtype=np.float64)
+    return out.reshape(np.shape(words))
+
+
+def gemm(dtype: str, A: np.ndarray, B: np.ndarray, C: np.ndarray, M: int, N: int, K: int,
+         lda: int, ldb: int, ldc: int, a_col: bool = False, b_col: bool = False, batch: int = 1,
+         sa: int | None = None, sb: int | None = None, sc: int | None = None,
+         nthreads: int | None = None):
+    """Full reference.  Returns (D_ref, S) for float types (float64, shape (batch, M, N)),
+    or D_ref (int64, shape (batch, M, N)) for int8.  Batch strides default to contiguous."""
+    _check_storage(dtype, A, B, C)
+    lib = _load()
+    sa = (K * lda if a_col else M * lda) if sa is None else sa
+    sb = (N * ldb if b_col else K * ldb) if sb is None else sb
+    sc = M * ldc if sc is None else sc
+    nthreads = default_threads() if nthreads is None else nthreads
+    if dtype == "i8":
+        D = np.zeros((batch, M, N), dtype=np.int64)
+        rc = lib.oracle_gemm_int8(_ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K, lda, ldb, ldc,
+                                  int(a_col), int(b_col), batch, sa, sb, sc, nthreads)
+        if rc:
+            raise ValueError("oracle_gemm_int8 rejected its arguments")
+        return D
+    D = np.zeros((batch, M, N), dtype=np.float64)
+    S = np.zeros((batch, M, N), dtype=np.float64)
+    rc = lib.oracle_gemm_float(DTYPES[dtype], _ptr(A), _ptr(B), _ptr(C.view(np.uint32)),
+                               _ptr(D), _ptr(S), M, N, K, lda, ldb, ldc,
+                               int(a_col), int(b_col), batch, sa, sb, sc, nthreads)
+    if rc:
+        raise ValueError("oracle_gemm_float rejected its arguments")
+    return D, S
+
+
+def gemm_points(dtype: str, A, B, C, pts: np.ndarray, M: int, N: int, K: int,
+                lda: int, ldb: int, ldc: int, a_col: bool = False, b_col: bool = False,
+                batch: int = 1, sa: int | None = None, sb: int | None = None, sc: int | None = None):
+    """Reference values at the listed (b, i, j) positions only.
+    Returns (D, S) float64 vectors for float types, or an int64 vector for int8."""
+    _check_storage(dtype, A, B, C)
+    lib = _load()
+    pts = np.ascontiguousarray(pts, dtype=np.int64).reshape(-1, 3)
+    n = pts.shape[0]
+    sa = (K * lda if a_col else M * lda) if sa is None else sa
+    sb = (N * ldb if b_col else K * ldb) if sb is None else sb
+    sc = M * ldc if sc is None else sc
+    D = np.zeros(n, dtype=np.float64)
+    S = np.zeros(n, dtype=np.float64)
+    Di = np.zeros(n, dtype=np.int64)
+    rc = lib.oracle_gemm_points(DTYPES[dtype], _ptr(A), _ptr(B), _ptr(C), _ptr(pts), n,
+                                _ptr(D), _ptr(S), _ptr(Di), M, N, K, lda, ldb, ldc,
+                                int(a_col), int(b_col), batch, sa, sb, sc)
+    if rc:
+        raise ValueError("oracle_gemm_points rejected its arguments")
+    return Di if dtype == "i8" else (D, S)
+
+
+def float_tolerance(K: int, S: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """Per-element bound |D - D_ref| <= 4*K*2^-24*S + 2^-24*|c| for fp16/bf16 inputs
+    accumulated in fp32, with C added once (the bound the fp paths are held to)."""
+    c = np.abs(np.asarray(C, dtype=np.float64))
+    return 4.0 * K * 2.0 ** -24 * np.asarray(S, dtype=np.float64) + 2.0 ** -24 * c

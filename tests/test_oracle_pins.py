@@ -1,0 +1,316 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself:
+library decoders, exact rational brute force, closed forms, and the properties a
+matrix product must have (identity, permutation, rank one, all ones, extremes,
+an empty reduction).  CPU only."""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+DT_FLOAT = ["f16", "bf16"]
+LAYOUTS = list(itertools.product([False, True], [False, True]))
+
+
+def lib_decode(dtype, bits):
+    """Library decoders, independent of the oracle's bit-field arithmetic."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    if dtype == "f16":
+        return bits.view(np.float16).astype(np.float64)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def logical(p: synth.Problem, b: int):
+    """Logical A (MxK), B (KxN), C (MxN) of batch b as storage-typed numpy views."""
+    A = p.A[b]
+    B = p.B[b]
+    A = A[:p.K, :p.M].T if p.a_col else A[:p.M, :p.K]
+    B = B[:p.N, :p.K].T if p.b_col else B[:p.K, :p.N]
+    C = p.C[b][:p.M, :p.N]
+    return A, B, C
+
+
+def run_oracle(p: synth.Problem, nthreads=3):
+    return oracle.gemm(p.dtype, p.A, p.B, p.C, **p.oracle_args(), nthreads=nthreads)
+
+
+# ---------------------------------------------------------------- decoders
+
+@pytest.mark.parametrize("dtype", DT_FLOAT)
+def test_decode_exhaustive(dtype):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.decode(dtype, bits)
+    ref = lib_decode(dtype, bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_f32_sample():
+    rng = np.random.default_rng(7)
+    words = rng.integers(0, 2 ** 32, size=20000, dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0, 0x80000000, 1, 0x807fffff, 0x00800000, 0x7f7fffff, 0x7f800000,
+                         0xff800000, 0x3f800000, 0x7fc00000], dtype=np.uint32)
+    words = np.concatenate([words, specials])
+    got = oracle.decode_f32(words)
+    ref = words.view(np.float32).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ------------------------------------------------------- exact brute force
+
+def exact_reference(p: synth.Problem):
+    """Exact rational D and S by brute force over Python Fractions (tiny sizes only)."""
+    out_d, out_s = [], []
+    for b in range(p.batch):
+        A, B, C = logical(p, b)
+        if p.dtype == "i8":
+            Af = [[int(v) for v in row] for row in A]
+            Bf = [[int(v) for v in row] for row in B]
+            Cf = [[int(v) for v in row] for row in C]
+        else:
+            Af = [[Fraction(float(v)) for v in row] for row in lib_decode(p.dtype, A)]
+            Bf = [[Fraction(float(v)) for v in row] for row in lib_decode(p.dtype, B)]
+            Cf = [[Fraction(float(v)) for v in row] for row in C.astype(np.float64)]
+        D = [[Cf[i][j] + sum(Af[i][k] * Bf[k][j] for k in range(p.K)) for j in range(p.N)]
+             for i in range(p.M)]
+        S = [[sum(abs(Af[i][k] * Bf[k][j]) for k in range(p.K)) for j in range(p.N)]
+             for i in range(p.M)]
+        out_d.append(D)
+        out_s.append(S)
+    return out_d, out_s
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_brute_force_tiny(dtype, a_col, b_col):
+    rng = np.random.default_rng(11)
+    for trial in range(6):
+        M, N, K = (int(x) for x in rng.integers(1, 9, size=3))
+        batch = int(rng.integers(1, 4))
+        pad = int(rng.integers(0, 3))
+        p = synth.make_problem(dtype, M, N, K, batch=batch, a_col=a_col, b_col=b_col, pad=pad,
+                               seed=1000 + trial, c_range=(-1.0, 1.0) if dtype != "i8" else (-1000, 1000))
+        ed, es = exact_reference(p)
+        if dtype == "i8":
+            D = run_oracle(p)
+            for b, i, j in itertools.product(range(batch), range(M), range(N)):
+                assert D[b, i, j] == ed[b][i][j]
+        else:
+            D, S = run_oracle(p)
+            for b, i, j in itertools.product(range(batch), range(M), range(N)):
+                s_exact = es[b][i][j]
+                assert abs(Fraction(D[b, i, j]) - ed[b][i][j]) <= K * Fraction(2) ** -53 * s_exact \
+                    + Fraction(2) ** -53 * abs(ed[b][i][j])
+                # products are exact in fp64, so S is exact up to the summation rounding
+                assert abs(Fraction(S[b, i, j]) - s_exact) <= K * Fraction(2) ** -53 * s_exact
+
+
+def test_points_match_brute_force():
+    for dtype, (a_col, b_col) in itertools.product(["f16", "bf16", "i8"], LAYOUTS):
+        p = synth.make_problem(dtype, 5, 7, 6, batch=2, a_col=a_col, b_col=b_col, pad=1, seed=77,
+                               c_range=(-1.0, 1.0) if dtype != "i8" else (-50, 50))
+        ed, es = exact_reference(p)
+        pts = np.array([(b, i, j) for b in range(2) for i in range(5) for j in range(7)])
+        r = oracle.gemm_points(p.dtype, p.A, p.B, p.C, pts, **p.oracle_args())
+        for n, (b, i, j) in enumerate(pts):
+            if dtype == "i8":
+                assert r[n] == ed[b][i][j]
+            else:
+                assert abs(Fraction(r[0][n]) - ed[b][i][j]) <= 6 * Fraction(2) ** -53 * (es[b][i][j] + 1)
+                assert abs(Fraction(r[1][n]) - es[b][i][j]) <= 6 * Fraction(2) ** -53 * es[b][i][j]
+
+
+# ------------------------------------------------------------ library matmul
+
+@pytest.mark.parametrize("dtype", DT_FLOAT)
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_against_numpy_matmul(dtype, a_col, b_col):
+    """Moderate shapes with padding and a batch: fp64 numpy matmul of the library-decoded
+    inputs agrees to fp64 summation accuracy."""
+    p = synth.make_problem(dtype, 37, 53, 71, batch=2, a_col=a_col, b_col=b_col, pad=3, seed=5)
+    D, S = run_oracle(p)
+    for b in range(2):
+        A, B, C = logical(p, b)
+        ref = lib_decode(dtype, A) @ lib_decode(dtype, B) + C.astype(np.float64)
+        sref = np.abs(lib_decode(dtype, A)) @ np.abs(lib_decode(dtype, B))
+        assert np.all(np.abs(D[b] - ref) <= 2 * p.K * 2.0 ** -52 * (sref + np.abs(ref)))
+        assert np.allclose(S[b], sref, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_int8_against_numpy_matmul(a_col, b_col):
+    p = synth.make_problem("i8", 29, 41, 300, batch=2, a_col=a_col, b_col=b_col, pad=2, seed=6,
+                           c_range=(-(1 << 20), 1 << 20))
+    D = run_oracle(p)
+    for b in range(2):
+        A, B, C = logical(p, b)
+        ref = A.astype(np.int64) @ B.astype(np.int64) + C.astype(np.int64)
+        assert np.array_equal(D[b], ref)
+
+
+# ------------------------------------------------------------ closed forms
+
+def bits_of(dtype, values):
+    v = np.asarray(values, dtype=np.float64)
+    if dtype == "f16":
+        return synth.f64_to_f16_bits(v)
+    if dtype == "bf16":
+        return synth.f32_to_bf16_bits(v.astype(np.float32))
+    return v.astype(np.int8)
+
+
+def build(dtype, A_log, B_log, C_log, a_col=False, b_col=False):
+    """Storage arrays for given logical matrices (tight leading dimensions, batch 1)."""
+    M, K = A_log.shape
+    N = B_log.shape[1]
+    A = bits_of(dtype, A_log.T if a_col else A_log)[None].copy()
+    B = bits_of(dtype, B_log.T if b_col else B_log)[None].copy()
+    C = np.asarray(C_log, dtype=np.int32 if dtype == "i8" else np.float32)[None].copy()
+    lda = M if a_col else K
+    ldb = K if b_col else N
+    return A, B, C, dict(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=N, a_col=a_col, b_col=b_col)
+
+
+def ref_result(dtype, A, B, C, args):
+    r = oracle.gemm(dtype, A, B, C, **args, nthreads=2)
+    return r if dtype == "i8" else r[0]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_identity(dtype, a_col, b_col):
+    """A*I + 0 = A and I*B + 0 = B exactly (the identity-B check input)."""
+    rng = np.random.default_rng(3)
+    M, K = 19, 23
+    if dtype == "i8":
+        A_log = rng.integers(-128, 128, size=(M, K)).astype(np.float64)
+    else:
+        A_log = lib_decode(dtype, bits_of(dtype, rng.uniform(-4, 4, size=(M, K))))
+    I = np.eye(K)
+    A, B, C, args = build(dtype, A_log, I, np.zeros((M, K)), a_col, b_col)
+    D = ref_result(dtype, A, B, C, args)[0]
+    assert np.array_equal(D, A_log)
+    A, B, C, args = build(dtype, np.eye(M), A_log, np.zeros((M, K)), a_col, b_col)
+    D = ref_result(dtype, A, B, C, args)[0]
+    assert np.array_equal(D, A_log)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_permutation(dtype, a_col, b_col):
+    """P*X permutes the rows of X; X*P permutes its columns -- exactly."""
+    rng = np.random.default_rng(4)
+    n = 17
+    perm = rng.permutation(n)
+    P = np.zeros((n, n))
+    P[np.arange(n), perm] = 1.0          # (P X)[i] = X[perm[i]]
+    X = rng.integers(-100, 100, size=(n, n)).astype(np.float64)
+    A, B, C, args = build(dtype, P, X, np.zeros((n, n)), a_col, b_col)
+    assert np.array_equal(ref_result(dtype, A, B, C, args)[0], X[perm])
+    A, B, C, args = build(dtype, X, P, np.zeros((n, n)), a_col, b_col)
+    inv = np.argsort(perm)               # (X P)[:, j] = X[:, inv[j]]
+    assert np.array_equal(ref_result(dtype, A, B, C, args)[0], X[:, inv])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_rank_one(dtype):
+    """A[i,k] = x_i, B[k,j] = y_j  =>  D = K*x_i*y_j + c_ij exactly."""
+    rng = np.random.default_rng(5)
+    M, N, K = 13, 11, 40
+    x = rng.integers(-4, 5, size=M).astype(np.float64)
+    y = rng.integers(-4, 5, size=N).astype(np.float64)
+    if dtype != "i8":
+        x = x * 2.0 ** rng.integers(-3, 3, size=M)
+        y = y * 2.0 ** rng.integers(-3, 3, size=N)
+    c = rng.integers(-9, 10, size=(M, N)).astype(np.float64)
+    A_log = np.repeat(x[:, None], K, axis=1)
+    B_log = np.repeat(y[None, :], K, axis=0)
+    A, B, C, args = build(dtype, A_log, B_log, c)
+    D = ref_result(dtype, A, B, C, args)[0]
+    assert np.array_equal(D, K * np.outer(x, y) + c)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_all_ones(dtype):
+    M, N, K = 9, 10, 300
+    c = np.arange(M * N).reshape(M, N) % 7 - 3.0
+    A, B, C, args = build(dtype, np.ones((M, K)), np.ones((K, N)), c)
+    D = ref_result(dtype, A, B, C, args)[0]
+    assert np.array_equal(D, K + c)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_all_ones_large_k_points(dtype):
+    """Every output equals K (+c) at the skinny workload's K = 65536."""
+    M = N = 4
+    K = 65536
+    A = bits_of(dtype, np.ones((1, M, K)))
+    B = bits_of(dtype, np.ones((1, K, N)))
+    C = (np.full((1, M, N), 3, dtype=np.int32) if dtype == "i8"
+         else np.full((1, M, N), 3.0, dtype=np.float32))
+    pts = np.array([(0, i, j) for i in range(M) for j in range(N)])
+    r = oracle.gemm_points(dtype, A, B, C, pts, M=M, N=N, K=K, lda=K, ldb=N, ldc=N)
+    vals = r if dtype == "i8" else r[0]
+    assert np.all(vals == K + 3)
+    if dtype != "i8":
+        assert np.all(r[1] == K)
+
+
+@pytest.mark.parametrize("bv,per_k", [(-128, 16384), (127, -16256)])
+def test_int8_extremes(bv, per_k):
+    M, N, K = 6, 5, 8192
+    c = np.arange(M * N).reshape(M, N) * 1000 - 7000
+    A, B, C, args = build("i8", np.full((M, K), -128.0), np.full((K, N), float(bv)), c)
+    D = ref_result("i8", A, B, C, args)[0]
+    assert np.array_equal(D, per_k * K + c)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_k_zero_gives_c(dtype):
+    p = synth.make_problem(dtype, 7, 9, 0, batch=2, seed=8,
+                           c_range=(-1.0, 1.0) if dtype != "i8" else (-100, 100))
+    r = run_oracle(p)
+    D = r if dtype == "i8" else r[0]
+    assert np.array_equal(D, p.C[:, :7, :9].astype(D.dtype))
+
+
+def test_thread_count_does_not_change_result():
+    p = synth.make_problem("bf16", 33, 29, 64, batch=3, seed=9, pad=1)
+    D1, S1 = oracle.gemm(p.dtype, p.A, p.B, p.C, **p.oracle_args(), nthreads=1)
+    D7, S7 = oracle.gemm(p.dtype, p.A, p.B, p.C, **p.oracle_args(), nthreads=7)
+    assert np.array_equal(D1, D7) and np.array_equal(S1, S7)
+
+
+# ------------------------------------------------------------ the tolerance
+
+def fp32_sequential(p: synth.Problem, drop_k=None):
+    """An fp32 round-to-nearest k-ordered accumulation, C added once at the end:
+    one legitimate way hardware may compute the float result."""
+    A, B, C = logical(p, 0)
+    Ad = lib_decode(p.dtype, A).astype(np.float32)
+    Bd = lib_decode(p.dtype, B).astype(np.float32)
+    acc = np.zeros((p.M, p.N), dtype=np.float32)
+    for k in range(p.K):
+        if k == drop_k:
+            continue
+        acc = acc + np.outer(Ad[:, k], Bd[k, :]).astype(np.float32)
+    return acc + C
+
+
+@pytest.mark.parametrize("dtype", DT_FLOAT)
+def test_tolerance_accepts_fp32_and_rejects_dropped_term(dtype):
+    p = synth.make_problem(dtype, 24, 24, 48, seed=12)
+    D, S = run_oracle(p)
+    tol = oracle.float_tolerance(p.K, S[0], p.C[0])
+    good = fp32_sequential(p).astype(np.float64)
+    assert np.all(np.abs(good - D[0]) <= tol)
+    bad = fp32_sequential(p, drop_k=17).astype(np.float64)
+    assert np.any(np.abs(bad - D[0]) > tol)
