@@ -1,0 +1,22 @@
+"""MI355X (gfx950) dense mixed-precision GEMM:  D = A*B + C.
+
+A thin ctypes binding over the C ABI in ``include/dmp_gemm.h`` (shared library
+``libdmp_gemm.so`` built from ``csrc/``).  Every arithmetic step runs in the
+library's HIP kernels; this module only marshals pointers, sizes and the
+stream.  PyTorch is used for device memory and streams only.
+
+    import torch, dense_mixed_precision_02_amd as dmp
+    A = torch.randn(4096, 4096, device="cuda").bfloat16()
+    B = torch.randn(4096, 4096, device="cuda").bfloat16().t()   # column-major view
+    C = torch.zeros(4096, 4096, device="cuda")
+    D = dmp.gemm(A, B, C)           # D = A @ B + C, fp32 accumulate
+"""
+from __future__ import annotations
+
+from .binding import (GEMM_A_COLMAJOR, GEMM_B_COLMAJOR, GEMM_BF16, GEMM_F16, GEMM_I8,
+                      GemmError, Handle, default_handle, gemm, lib_path, load_library,
+                      plan_label, status_string, EXPORTED_SYMBOLS)
+
+__all__ = ["GEMM_A_COLMAJOR", "GEMM_B_COLMAJOR", "GEMM_BF16", "GEMM_F16", "GEMM_I8",
+           "GemmError", "Handle", "default_handle", "gemm", "lib_path", "load_library",
+           "plan_label", "status_string", "EXPORTED_SYMBOLS"]

@@ -1,0 +1,98 @@
+// aux_kernels.hpp -- the any-alignment MFMA kernel, the split-K reduction and
+// the K == 0 copy.
+#pragma once
+#include "common.hpp"
+
+namespace dmp {
+
+struct GenericArgs {
+    const void *A, *B, *C;
+    void *D;
+    int64_t M, N, K;
+    int64_t a_rs, a_ks, b_ks, b_cs;  // element strides: A[i][k] = A[i*a_rs + k*a_ks], B[k][j] = B[k*b_ks + j*b_cs]
+    int64_t ldc, sA, sB, sC;
+    int tiles_m, tiles_n;
+};
+
+// Element loads for the any-alignment path (no vector loads, no alignment
+// assumption beyond the element's own).
+__device__ static inline uint32_t load_elem(const uint16_t *p) { return *p; }
+__device__ static inline uint32_t load_elem(const int8_t *p) { return (uint8_t)*p; }
+
+// One wave per 32x32 output tile.  Fragments come straight from global memory
+// element by element, so any pointer alignment, leading dimension and K work;
+// the MFMA, its fragment layout (lane L: row or column L%32, K elements
+// G*(L/32) .. G*(L/32)+G-1 of each step) and the epilogue are those of the
+// tiled kernel.  Used when the 16-byte granule path does not apply.
+template <class DT>
+__global__ __launch_bounds__(64) void generic_gemm(const GenericArgs p) {
+    using elem = typename DT::elem;
+    using acc_t = typename DT::acc;
+    using accv = typename DT::accv;
+    constexpr int G = DT::G;
+    constexpr int EPW = 4 / DT::ESZ;  // elements per 32-bit word
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int b = blockIdx.x / tiles;
+    const int t = blockIdx.x - b * tiles;
+    const int64_t m0 = (int64_t)(t / p.tiles_n) * 32, n0 = (int64_t)(t % p.tiles_n) * 32;
+    const int lane = threadIdx.x;
+    const elem *A = (const elem *)p.A + b * p.sA;
+    const elem *B = (const elem *)p.B + b * p.sB;
+    const int64_t row = m0 + (lane & 31), col = n0 + (lane & 31);
+    const int kh = (lane >> 5) * G;
+    accv acc = accv{};
+    for (int64_t k0 = 0; k0 < p.K; k0 += 2 * G) {
+        intx4 fa, fb;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t wa = 0, wb = 0;
+#pragma unroll
+            for (int q = 0; q < EPW; ++q) {
+                const int64_t k = k0 + kh + w * EPW + q;
+                const uint32_t va = (row < p.M && k < p.K) ? load_elem(A + row * p.a_rs + k * p.a_ks) : 0u;
+                const uint32_t vb = (col < p.N && k < p.K) ? load_elem(B + k * p.b_ks + col * p.b_cs) : 0u;
+                wa |= va << (q * 8 * DT::ESZ);
+                wb |= vb << (q * 8 * DT::ESZ);
+            }
+            fa[w] = (int)wa;
+            fb[w] = (int)wb;
+        }
+        acc = DT::mfma(fa, fb, acc);
+    }
+    const acc_t *Cb = (const acc_t *)p.C + b * p.sC;
+    acc_t *Db = (acc_t *)p.D + b * p.sC;
+    const int64_t c = n0 + (lane & 31);
+    if (c < p.N) {
+#pragma unroll
+        for (int G2 = 0; G2 < 16; ++G2) {
+            const int64_t r = m0 + 8 * (G2 >> 2) + 4 * (lane >> 5) + (G2 & 3);
+            if (r < p.M) Db[r * p.ldc + c] = add_acc(acc[G2], Cb[r * p.ldc + c]);
+        }
+    }
+}
+
+// Split-K reduction: D = (P_0 + P_1 + ... + P_{S-1}) + C, summed in that fixed
+// order (so the result is the same on every run), with C added once at the end.
+// With S == 0 it copies C to D.  W holds S*batch dense M x N partial tiles.
+template <class T>
+__global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, const T *C, T *D,
+                                                     int64_t M, int64_t N, int64_t ldc, int64_t batch,
+                                                     int S) {
+    const int64_t MN = M * N;
+    const int64_t total = MN * batch;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = e / MN, rem = e - b * MN;
+        const int64_t i = rem / N, j = rem - i * N;
+        const int64_t idx = b * M * ldc + i * ldc + j;
+        if (S == 0) {
+            D[idx] = C[idx];
+            continue;
+        }
+        T s = W[e];
+        for (int q = 1; q < S; ++q) s = add_acc(s, W[(int64_t)q * total + e]);
+        D[idx] = add_acc(s, C[idx]);
+    }
+}
+
+}  // namespace dmp

@@ -1,0 +1,353 @@
+// gemm_api.hip -- the C ABI declared in include/dmp_gemm.h: argument checks,
+// kernel-path selection, workspace management and launches on the caller's
+// stream.  Host code only; the kernels live in tile_gemm.hpp and aux_kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/dmp_gemm.h"
+#include "aux_kernels.hpp"
+#include "tile_gemm.hpp"
+
+using namespace dmp;
+
+struct gemm_handle {
+    int device = 0;
+    int num_cus = 0;
+    void *ws = nullptr;   // split-K partials, grown on demand
+    size_t ws_bytes = 0;
+};
+
+namespace {
+
+// Workgroup tile shapes of the tiled kernel (4 waves each, 2 x 2).
+enum Cfg { CFG_L = 0, CFG_M = 1, CFG_S = 2, CFG_GENERIC = 3 };
+constexpr int CFG_EDGE[3] = {256, 128, 64};
+
+struct Plan {
+    int cfg = CFG_GENERIC;
+    int splits = 1;
+    int64_t k_chunk = 0;
+    int tiles_m = 0, tiles_n = 0;
+    int64_t grid = 0;
+    bool reduce = false;     // second launch: fixed-order sum of partials + C
+    bool copy_only = false;  // K == 0: D = C
+    size_t ws_needed = 0;
+};
+
+int elem_size(int dtype) { return dtype == GEMM_I8 ? 1 : 2; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const void *D,
+             int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+             unsigned flags, int64_t batch, bool check_ptrs) {
+    if (!h) return GEMM_ERR_INVALID_ARG;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) return GEMM_ERR_INVALID_ARG;
+    if (flags & ~(unsigned)(GEMM_A_COLMAJOR | GEMM_B_COLMAJOR)) return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
+    const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
+    // A and B are not read when K == 0, so their leading dimensions are free then
+    if (K > 0 && lda < std::max<int64_t>(1, a_col ? M : K)) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && ldb < std::max<int64_t>(1, b_col ? K : N)) return GEMM_ERR_INVALID_ARG;
+    if (ldc < std::max<int64_t>(1, N)) return GEMM_ERR_INVALID_ARG;
+    // grid dimensions and element indices are kept well inside their integer types
+    if (M > (1ll << 31) - 1024 || N > (1ll << 31) - 1024 || batch > (1ll << 30))
+        return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    if (!check_ptrs) return GEMM_OK;
+    if (!C || !D) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+    const uintptr_t es = (uintptr_t)elem_size(dtype);
+    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4) || ((uintptr_t)D % 4))
+        return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Can the 16-byte granule path handle these operands?  Every granule must be
+// 16-byte aligned and wholly inside or wholly outside the matrix, and per-lane
+// byte offsets must fit 31 bits.
+bool granule_ok(const void *A, const void *B, int64_t M, int64_t N, int64_t K, int64_t lda,
+                int64_t ldb, int dtype, bool a_col, bool b_col, bool check_ptrs) {
+    const int es = elem_size(dtype);
+    const int G = 16 / es;
+    if (check_ptrs && (!aligned16(A) || !aligned16(B))) return false;
+    if ((lda * es) % 16 || (ldb * es) % 16) return false;
+    const bool a_k = !a_col, b_k = b_col;
+    // the contiguous extent of each operand is a whole number of granules, so no
+    // granule reaches past the last element of a row or column
+    if ((a_k || b_k) && K % G) return false;
+    if ((!a_k && M % G) || (!b_k && N % G)) return false;
+    const int64_t kt = 128 / es;
+    const int64_t lim = (1ll << 31) - (1ll << 22);
+    // offsets inside one k-tile: up to 256 rows (K-contig) or kt k-rows (MN-contig)
+    const int64_t span_a = (a_k ? 256 * lda : kt * lda) * es;
+    const int64_t span_b = (b_k ? 256 * ldb : kt * ldb) * es;
+    return span_a < lim && span_b < lim;
+}
+
+Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int dtype, unsigned flags, int64_t batch, bool check_ptrs) {
+    Plan P;
+    const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
+    if (K == 0) {
+        P.copy_only = true;
+        return P;
+    }
+    const int es = elem_size(dtype);
+    const int64_t kt = 128 / es;
+    if (!granule_ok(A, B, M, N, K, lda, ldb, dtype, a_col, b_col, check_ptrs)) {
+        P.cfg = CFG_GENERIC;
+        P.tiles_m = (int)cdiv(M, 32);
+        P.tiles_n = (int)cdiv(N, 32);
+        P.grid = (int64_t)P.tiles_m * P.tiles_n * batch;
+        return P;
+    }
+    const int64_t cus = h->num_cus > 0 ? h->num_cus : 256;
+    auto tiles = [&](int cfg) {
+        return cdiv(M, CFG_EDGE[cfg]) * cdiv(N, CFG_EDGE[cfg]) * batch;
+    };
+    // Fraction of a config's tile area that is inside the matrix.
+    auto useful = [&](int cfg) {
+        const double e = CFG_EDGE[cfg];
+        return (double)M * (double)N / ((double)cdiv(M, CFG_EDGE[cfg]) * e *
+                                        (double)cdiv(N, CFG_EDGE[cfg]) * e);
+    };
+    const int64_t nkt = cdiv(K, kt);
+    // Largest tile that wastes at most a quarter of its area to the edges.
+    int cfg = CFG_S;
+    for (int c = CFG_L; c <= CFG_S; ++c)
+        if (useful(c) >= 0.75) {
+            cfg = c;
+            break;
+        }
+    int64_t splits = 1;
+    if (tiles(cfg) < cus) {
+        // Under one workgroup per CU.  A long K is split (each split keeps at
+        // least 8 k-tiles) so the large tile's low traffic per flop is kept;
+        // a short K instead moves to smaller tiles.
+        const int64_t s = std::min(cus / tiles(cfg), nkt / 8);
+        if (s >= 2) {
+            splits = s;
+        } else {
+            while (cfg < CFG_S && tiles(cfg) < cus && useful(cfg + 1) >= 0.75) ++cfg;
+        }
+    }
+    const int e = CFG_EDGE[cfg];
+    P.cfg = cfg;
+    P.tiles_m = (int)cdiv(M, e);
+    P.tiles_n = (int)cdiv(N, e);
+    P.k_chunk = cdiv(nkt, splits) * kt;
+    P.splits = (int)cdiv(K, P.k_chunk);  // no empty splits
+    P.grid = (int64_t)P.tiles_m * P.tiles_n * batch * P.splits;
+    if (P.splits > 1) {
+        P.reduce = true;
+        P.ws_needed = (size_t)P.splits * (size_t)batch * (size_t)M * (size_t)N * 4u;
+    }
+    return P;
+}
+
+const char *cfg_name(int cfg) {
+    switch (cfg) {
+    case CFG_L: return "tile256x256";
+    case CFG_M: return "tile128x128";
+    case CFG_S: return "tile64x64";
+    default: return "generic32x32";
+    }
+}
+
+const char *dtype_name(int d) { return d == GEMM_F16 ? "f16" : d == GEMM_BF16 ? "bf16" : "i8"; }
+
+template <class DT, int BM, int BN, bool AK, bool BKC>
+hipError_t launch_tile(const TileArgs &a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((tile_gemm<DT, BM, BN, 2, 2, AK, BKC>), dim3((unsigned)grid), dim3(256), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+template <class DT, int E>
+hipError_t launch_tile_layout(const TileArgs &a, bool a_col, bool b_col, int64_t grid,
+                              hipStream_t s) {
+    // AK: A is K-contiguous (row-major); BKC: B is K-contiguous (col-major)
+    if (!a_col && b_col) return launch_tile<DT, E, E, true, true>(a, grid, s);
+    if (!a_col && !b_col) return launch_tile<DT, E, E, true, false>(a, grid, s);
+    if (a_col && b_col) return launch_tile<DT, E, E, false, true>(a, grid, s);
+    return launch_tile<DT, E, E, false, false>(a, grid, s);
+}
+
+template <class DT>
+hipError_t launch_cfg(int cfg, const TileArgs &a, bool a_col, bool b_col, int64_t grid,
+                      hipStream_t s) {
+    switch (cfg) {
+    case CFG_L: return launch_tile_layout<DT, 256>(a, a_col, b_col, grid, s);
+    case CFG_M: return launch_tile_layout<DT, 128>(a, a_col, b_col, grid, s);
+    default: return launch_tile_layout<DT, 64>(a, a_col, b_col, grid, s);
+    }
+}
+
+int64_t reduce_grid(int64_t elems) {
+    return std::max<int64_t>(1, std::min<int64_t>(cdiv(elems, 256), 256 * 64));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *gemm_status_string(int status) {
+    switch (status) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+    case GEMM_ERR_UNSUPPORTED_DEVICE: return "GEMM_ERR_UNSUPPORTED_DEVICE";
+    case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    default: return "GEMM_ERR_UNKNOWN";
+    }
+}
+
+int gemm_create(gemm_handle_t *out) {
+    if (!out) return GEMM_ERR_INVALID_ARG;
+    *out = nullptr;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
+    gemm_handle *h = new (std::nothrow) gemm_handle;
+    if (!h) return GEMM_ERR_ALLOC;
+    h->device = dev;
+    h->num_cus = prop.multiProcessorCount;
+    *out = h;
+    return GEMM_OK;
+}
+
+int gemm_destroy(gemm_handle_t h) {
+    if (!h) return GEMM_ERR_INVALID_ARG;
+    int rc = GEMM_OK;
+    if (h->ws) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) rc = GEMM_ERR_HIP;
+        if (hipSetDevice(h->device) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(h->ws) != hipSuccess)
+            rc = GEMM_ERR_HIP;
+        (void)hipSetDevice(cur);
+    }
+    delete h;
+    return rc;
+}
+
+int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+              int64_t ldc, int dtype, unsigned flags, int64_t batch, char *label, size_t label_len) {
+    gemm_handle host_only;  // h == NULL: plan for a 256-CU device without touching HIP
+    host_only.num_cus = 256;
+    if (!h) h = &host_only;
+    int rc = validate(h, nullptr, nullptr, nullptr, nullptr, M, N, K, lda, ldb, ldc, dtype, flags,
+                      batch, false);
+    if (rc != GEMM_OK) return rc;
+    if (!label || label_len == 0) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || batch == 0) {
+        std::snprintf(label, label_len, "noop");
+        return GEMM_OK;
+    }
+    const Plan P = make_plan(h, nullptr, nullptr, M, N, K, lda, ldb, dtype, flags, batch, false);
+    if (P.copy_only) {
+        std::snprintf(label, label_len, "copy_c k=0");
+        return GEMM_OK;
+    }
+    std::snprintf(label, label_len, "%s %s a:%s b:%s splitk=%d grid=%lld", cfg_name(P.cfg),
+                  dtype_name(dtype), (flags & GEMM_A_COLMAJOR) ? "col" : "row",
+                  (flags & GEMM_B_COLMAJOR) ? "col" : "row", P.splits, (long long)P.grid);
+    return GEMM_OK;
+}
+
+int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
+             int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+             unsigned flags, int64_t batch, void *stream) {
+    int rc = validate(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, true);
+    if (rc != GEMM_OK) return rc;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
+    const int64_t sA = (a_col ? K : M) * lda, sB = (b_col ? N : K) * ldb, sC = M * ldc;
+    const Plan P = make_plan(h, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
+    if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
+
+    if (P.copy_only) {
+        const int64_t elems = M * N * batch;
+        if (dtype == GEMM_I8)
+            hipLaunchKernelGGL(splitk_reduce<int32_t>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0,
+                               s, nullptr, (const int32_t *)C, (int32_t *)D, M, N, ldc, batch, 0);
+        else
+            hipLaunchKernelGGL(splitk_reduce<float>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
+                               nullptr, (const float *)C, (float *)D, M, N, ldc, batch, 0);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    }
+
+    if (P.cfg == CFG_GENERIC) {
+        GenericArgs g;
+        g.A = A; g.B = B; g.C = C; g.D = D;
+        g.M = M; g.N = N; g.K = K;
+        g.a_rs = a_col ? 1 : lda;
+        g.a_ks = a_col ? lda : 1;
+        g.b_ks = b_col ? 1 : ldb;
+        g.b_cs = b_col ? ldb : 1;
+        g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
+        g.tiles_m = P.tiles_m; g.tiles_n = P.tiles_n;
+        const dim3 grid((unsigned)P.grid), blk(64);
+        if (dtype == GEMM_F16) hipLaunchKernelGGL(generic_gemm<F16>, grid, blk, 0, s, g);
+        else if (dtype == GEMM_BF16) hipLaunchKernelGGL(generic_gemm<BF16>, grid, blk, 0, s, g);
+        else hipLaunchKernelGGL(generic_gemm<I8>, grid, blk, 0, s, g);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    }
+
+    if (P.reduce && h->ws_bytes < P.ws_needed) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return GEMM_ERR_INVALID_ARG;
+        if (h->ws) {
+            // the old workspace may still be read by queued work on some stream
+            if (hipDeviceSynchronize() != hipSuccess) return GEMM_ERR_HIP;
+            if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
+            h->ws = nullptr;
+            h->ws_bytes = 0;
+        }
+        if (hipMalloc(&h->ws, P.ws_needed) != hipSuccess) {
+            h->ws = nullptr;
+            (void)hipGetLastError();
+            return GEMM_ERR_ALLOC;
+        }
+        h->ws_bytes = P.ws_needed;
+    }
+
+    TileArgs t;
+    t.A = A; t.B = B; t.C = C; t.D = D; t.W = h->ws;
+    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldb; t.ldc = ldc;
+    t.sA = sA; t.sB = sB; t.sC = sC;
+    t.k_chunk = P.k_chunk;
+    t.tiles_m = P.tiles_m; t.tiles_n = P.tiles_n;
+    t.batch = (int)batch; t.splits = P.splits;
+    t.partial = P.reduce ? 1 : 0;
+    hipError_t e;
+    if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_col, P.grid, s);
+    else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_col, P.grid, s);
+    else e = launch_cfg<I8>(P.cfg, t, a_col, b_col, P.grid, s);
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    if (P.reduce) {
+        const int64_t elems = M * N * batch;
+        if (dtype == GEMM_I8)
+            hipLaunchKernelGGL(splitk_reduce<int32_t>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0,
+                               s, (const int32_t *)h->ws, (const int32_t *)C, (int32_t *)D, M, N, ldc,
+                               batch, P.splits);
+        else
+            hipLaunchKernelGGL(splitk_reduce<float>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
+                               (const float *)h->ws, (const float *)C, (float *)D, M, N, ldc, batch,
+                               P.splits);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+    }
+    return GEMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,313 @@
+// tile_gemm.hpp -- the tiled MFMA GEMM kernel for gfx950.
+//
+// One workgroup owns a BM x BN tile of D (of one batch entry, and one K range
+// when split-K is on).  Per 128-byte K panel ("k-tile": 64 fp16/bf16 or 128
+// int8 elements) it
+//   1. copies the A panel (BM x k-tile) and the B panel (k-tile x BN) from global
+//      memory straight into LDS with 16-byte buffer loads that bypass registers
+//      (out-of-range granules come back as zero), into the LDS buffer that the
+//      MFMAs are not reading (two buffers, alternating);
+//   2. reads 16-byte fragments from the other buffer and issues 32x32 MFMAs
+//      (the K-panel accumulation of the pages: "CDNA2 dense MFMA builtins",
+//      section "Naming convention" -- each instruction adds one K step of an A
+//      panel times a B panel to an M x N accumulator tile, the caller loops K).
+// After the K loop the epilogue adds C once and writes D (or, under split-K,
+// writes the raw partial tile to a workspace).
+//
+// Operand storage.  Both operands are seen as "R rows x K": A is M x K and B is
+// (B^T) N x K.  An operand is K-contiguous (A row-major, B col-major) or
+// MN-contiguous (A col-major, B row-major).
+//  * K-contiguous panels are stored in LDS as R rows of 128 bytes; the 16-byte
+//    granule g of row r sits at slot g ^ swz(r), which makes the fragment reads
+//    (32 lanes on 32 consecutive rows, same granule) hit distinct banks.
+//  * MN-contiguous panels are stored in 128-byte blocks, each holding 4 k-rows
+//    x 16 rows (16-bit types) or 8 k-rows x 16 rows (int8).  A fragment is then
+//    read with the gfx950 LDS transpose loads: a group of 16 lanes reads one
+//    whole block (128 contiguous bytes) and every lane receives 4 (or 8)
+//    consecutive k values of its own row -- the K-contiguous register layout the
+//    MFMA needs.
+#pragma once
+#include "common.hpp"
+
+namespace dmp {
+
+struct TileArgs {
+    const void *A, *B, *C;
+    void *D, *W;
+    int64_t M, N, K, lda, ldb, ldc;
+    int64_t sA, sB, sC;      // batch strides in elements
+    int64_t k_chunk;         // K elements per split (multiple of the k-tile)
+    int tiles_m, tiles_n, batch, splits;
+    int partial;             // 1: write raw partials to W (split-K), 0: D = acc + C
+};
+
+// Row swizzle of the K-contiguous LDS layout.  Any 8 consecutive rows (and the
+// even/odd rows of any 16) map to distinct 16-byte slots modulo 128 (256) bytes.
+__device__ static inline int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <class DT, int R, int NW, bool KCONTIG>
+struct Operand {
+    // R rows per tile, NW waves in the workgroup.
+    static constexpr int ESZ = DT::ESZ;
+    static constexpr int G = DT::G;
+    static constexpr int KT = 128 / ESZ;            // k-tile in elements
+    static constexpr int BYTES = R * 128;           // one LDS buffer
+    static constexpr int CHUNKS = BYTES / 1024;     // 1 KB per wave-wide load
+    static_assert(CHUNKS % NW == 0, "chunks must split evenly over waves");
+    static constexpr int CPW = CHUNKS / NW;         // chunks per wave
+    static constexpr int KB = (ESZ == 2) ? 4 : 8;   // k-rows per 128-byte block (MN-contig)
+    static_assert((NW * 8) % (R / 16) == 0, "MN-contig chunk stride must be whole block rows");
+
+    // Chunk j of this wave is chunk c = j*NW + wave of the tile.  Successive
+    // chunks of one wave differ by a fixed step: 8*NW rows (K-contig) or
+    // KB*(8*NW)/(R/16) k-rows (MN-contig), so one offset per lane suffices.
+    int off0;      // byte offset of this lane's granule in chunk j = 0
+    int row_or_k;  // K-contig: row of chunk 0 (rows step by 8*NW); MN-contig: k of chunk 0
+    int fixed;     // K-contig: k offset of the granule; MN-contig: row offset of the granule
+    int step;      // byte offset between successive chunks (uniform)
+
+    __device__ void init(int wave, int lane, int64_t ld, int row0, int64_t Rtot) {
+        if (KCONTIG) {
+            const int r = wave * 8 + (lane >> 3);
+            const int g = (lane & 7) ^ swz(r);  // swz(r + 8*NW*j) == swz(r): 8*NW is a multiple of 16
+            off0 = (int)(r * ld + g * G) * ESZ;
+            row_or_k = row0 + r;
+            fixed = g * G;
+            step = (int)(8 * NW * ld) * ESZ;
+        } else {
+            const int bid = wave * 8 + (lane >> 3);
+            const int kb = bid / (R / 16), mb = bid % (R / 16);
+            int k, mn;
+            if (ESZ == 2) {
+                k = kb * 4 + ((lane & 7) >> 1);
+                mn = mb * 16 + (lane & 1) * 8;
+            } else {
+                k = kb * 8 + (lane & 7);
+                mn = mb * 16;
+            }
+            off0 = (int)(k * ld + mn) * ESZ;
+            row_or_k = k;
+            fixed = row0 + mn;
+            step = (int)(KSTEP * ld) * ESZ;
+        }
+        (void)Rtot;
+    }
+    static constexpr int KSTEP = KB * (8 * NW) / (R / 16);  // MN-contig: k-rows between chunks
+
+    // Issue this wave's share of the copy of one k-tile into LDS buffer `lds`.
+    // base: element (row0, k0) of the operand.  kleft: valid k elements from k0.
+    __device__ void issue(const void *base, DMP_LDS char *lds, int wave, int kleft, int64_t Rtot) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+            const int c = j * NW + wave;
+            bool ok;
+            if (KCONTIG) ok = (row_or_k + 8 * NW * j < Rtot) && (fixed < kleft);
+            else ok = (fixed < Rtot) && (row_or_k + KSTEP * j < kleft);
+            load_granule_to_lds(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
+        }
+    }
+
+    // 16-byte fragment for MFMA step s (2 granules of K) of rows [rbase, rbase+32):
+    // lane L gets row rbase + L%32 and K granule 2s + L/32 of the k-tile.
+    __device__ static intx4 frag(const DMP_LDS char *lds, int rbase, int s, int lane) {
+        if (KCONTIG) {
+            const int row = rbase + (lane & 31);
+            const int g = 2 * s + (lane >> 5);
+            return *(const DMP_LDS intx4 *)(lds + row * 128 + ((g ^ swz(row)) << 4));
+        } else {
+            const int grp = lane >> 4, j = lane & 15, h = grp >> 1;
+            const int mn = rbase + 16 * (grp & 1);
+            intx4 out;
+            if (ESZ == 2) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int k = s * 16 + 8 * h + 4 * t;  // multiple of 4: first row of a block
+                    const int addr = ((k >> 2) * (R / 16) + (mn >> 4)) * 128 + j * 8;
+                    shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (DMP_LDS shortx4 *)(lds + addr));
+                    intx2 w = __builtin_bit_cast(intx2, v);
+                    out[2 * t] = w[0];
+                    out[2 * t + 1] = w[1];
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int k = s * 32 + 16 * h + 8 * t;  // multiple of 8: first row of a block
+                    const int addr = ((k >> 3) * (R / 16) + (mn >> 4)) * 128 + j * 8;
+                    intx2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DMP_LDS intx2 *)(lds + addr));
+                    out[2 * t] = w[0];
+                    out[2 * t + 1] = w[1];
+                }
+            }
+            return out;
+        }
+    }
+
+    // Pointer to element (row0, k0) of the operand.
+    __device__ static const char *tile_base(const void *X, int64_t ld, int64_t row0, int64_t k0) {
+        const char *p = (const char *)X;
+        return KCONTIG ? p + (row0 * ld + k0) * ESZ : p + (k0 * ld + row0) * ESZ;
+    }
+};
+
+// The two LDS buffers are distinct arrays so that the compiler can tell that
+// copies into one never alias fragment reads from the other.
+template <class DT, int BM, int BN, int WM, int WN, bool AK, bool BKC>
+__global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+    constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
+    constexpr int KT = 128 / DT::ESZ;            // k-tile in elements
+    constexpr int STEPS = 4;                     // 32x32 MFMA steps per k-tile
+    using OpA = Operand<DT, BM, NW, AK>;
+    using OpB = Operand<DT, BN, NW, BKC>;
+    using acc_t = typename DT::acc;
+    using accv = typename DT::accv;
+
+    __shared__ __attribute__((aligned(1024))) char lds_a0[OpA::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_b0[OpB::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_a1[OpA::BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds_b1[OpB::BYTES];
+
+    // ---- which tile: XCD-aware remap, then grouped order ----------------------
+    // Workgroup i is dispatched to XCD i % 8.  Renumber so that consecutive tile
+    // ids share an XCD (and its L2), then walk tiles in groups of 4 tile-rows.
+    int wg = blockIdx.x;
+    {
+        const int total = gridDim.x, per = total / 8;
+        if (wg < per * 8) wg = (wg % 8) * per + wg / 8;
+    }
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int prob = wg / tiles;
+    int t = wg - prob * tiles;
+    const int split = prob / p.batch, b = prob - split * p.batch;
+    constexpr int GM = 4;
+    const int group = t / (GM * p.tiles_n);
+    const int first_m = group * GM;
+    const int gm = min(p.tiles_m - first_m, GM);
+    t -= group * GM * p.tiles_n;
+    const int tm = first_m + t % gm, tn = t / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t k_begin = (int64_t)split * p.k_chunk;
+    const int64_t k_end = min(p.K, k_begin + p.k_chunk);
+    const int nkt = k_end > k_begin ? (int)((k_end - k_begin + KT - 1) / KT) : 0;
+
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave / WN, wn = wave % WN;
+
+    const char *Ab = (const char *)p.A + (int64_t)b * p.sA * DT::ESZ;
+    const char *Bb = (const char *)p.B + (int64_t)b * p.sB * DT::ESZ;
+
+    OpA opa;
+    OpB opb;
+    opa.init(wave, lane, p.lda, (int)m0, p.M);
+    opb.init(wave, lane, p.ldb, (int)n0, p.N);
+
+    accv acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = accv{};
+
+    // An odd k-tile count is made even by a leading k-tile that is all zeros
+    // (every granule out of range), so the loop below has a single exit.
+    const int ntiles = nkt + (nkt & 1);
+    const int64_t k_first = k_begin - (int64_t)(nkt & 1) * KT;
+    auto stage = [&](int kt, DMP_LDS char *la, DMP_LDS char *lb) {
+        const int64_t k0 = k_first + (int64_t)kt * KT;
+        const int kleft = k0 < k_begin ? 0 : (int)min<int64_t>(k_end - k0, KT);
+        opa.issue(OpA::tile_base(Ab, p.lda, m0, k0), la, wave, kleft, p.M);
+        opb.issue(OpB::tile_base(Bb, p.ldb, n0, k0), lb, wave, kleft, p.N);
+    };
+    // Fragments for step s of the k-tile held in (la, lb).
+    auto read = [&](intx4 (&fa)[TM], intx4 (&fb)[TN], const DMP_LDS char *la,
+                    const DMP_LDS char *lb, int s) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = OpA::frag(la, wm * WTM + i * 32, s, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = OpB::frag(lb, wn * WTN + j * 32, s, lane);
+    };
+    auto mma = [&](const intx4 (&fa)[TM], const intx4 (&fb)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = DT::mfma(fa[i], fb[j], acc[i][j]);
+    };
+
+    DMP_LDS char *LA[2] = {(DMP_LDS char *)lds_a0, (DMP_LDS char *)lds_a1};
+    DMP_LDS char *LB[2] = {(DMP_LDS char *)lds_b0, (DMP_LDS char *)lds_b1};
+
+    // Software pipeline.  Fragments of step s+1 are read while the MFMAs of step
+    // s run.  Before the last step of k-tile kt every wave waits for k-tile kt+1
+    // to land and for its own reads of kt to finish; after that barrier the
+    // buffer of kt is free and receives k-tile kt+2, and step 0 of kt+1 is read
+    // from the other buffer while the MFMAs of step 3 of kt run.
+    intx4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    auto ktile = [&](int kt, int cur) {
+        read(fa1, fb1, LA[cur], LB[cur], 1);
+        mma(fa0, fb0);
+        read(fa0, fb0, LA[cur], LB[cur], 2);
+        mma(fa1, fb1);
+        read(fa1, fb1, LA[cur], LB[cur], 3);
+        mma(fa0, fb0);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + 2 < ntiles) stage(kt + 2, LA[cur], LB[cur]);
+        if (kt + 1 < ntiles) read(fa0, fb0, LA[cur ^ 1], LB[cur ^ 1], 0);
+        mma(fa1, fb1);
+    };
+    if (nkt > 0) {
+        stage(0, LA[0], LB[0]);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (ntiles > 1) stage(1, LA[1], LB[1]);
+        read(fa0, fb0, LA[0], LB[0], 0);
+        // two k-tiles per trip so that each buffer is named statically
+        for (int kt = 0; kt < ntiles; kt += 2) {
+            ktile(kt, 0);
+            ktile(kt + 1, 1);
+        }
+    }
+
+    // ---- epilogue -----------------------------------------------------------
+    // Accumulator register G of lane L in a 32x32 tile holds row
+    // 8*(G/4) + 4*(L/32) + G%4 and column L%32.
+    const int64_t rbase = m0 + wm * WTM + 4 * (lane >> 5);
+    const int64_t cbase = n0 + wn * WTN + (lane & 31);
+    if (p.partial) {
+        acc_t *Wb = (acc_t *)p.W + ((int64_t)split * p.batch + b) * p.M * p.N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = cbase + j * 32;
+                if (col >= p.N) continue;
+#pragma unroll
+                for (int G = 0; G < 16; ++G) {
+                    const int64_t row = rbase + i * 32 + 8 * (G >> 2) + (G & 3);
+                    if (row < p.M) Wb[row * p.N + col] = acc[i][j][G];
+                }
+            }
+    } else {
+        const acc_t *Cb = (const acc_t *)p.C + (int64_t)b * p.sC;
+        acc_t *Db = (acc_t *)p.D + (int64_t)b * p.sC;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int64_t col = cbase + j * 32;
+                if (col >= p.N) continue;
+#pragma unroll
+                for (int G = 0; G < 16; ++G) {
+                    const int64_t row = rbase + i * 32 + 8 * (G >> 2) + (G & 3);
+                    if (row < p.M) {
+                        const int64_t idx = row * p.ldc + col;
+                        Db[idx] = add_acc(acc[i][j][G], Cb[idx]);
+                    }
+                }
+            }
+    }
+}
+
+}  // namespace dmp

@@ -1,0 +1,115 @@
+/*
+ * dmp_gemm.h -- C ABI of the gfx950 (MI355X) dense mixed-precision GEMM library.
+ *
+ * Operation (pages: "CDNA2 dense MFMA builtins", section "Naming convention",
+ * and "RDNA3 dense WMMA builtins", builtin reference): one MFMA step adds the
+ * contribution of a K-wide panel of A (M x K) and of B (K x N) to an M x N
+ * accumulator tile; the caller loops over K and the result of a step is
+ * srcA x srcB + srcC.  This library runs the whole loop on the GPU and computes,
+ * for every batch index b < batch,
+ *
+ *         D_b = A_b * B_b + C_b
+ *
+ * with the input types and accumulators below.  C is added once, after the
+ * whole K reduction (an fp32 round-to-nearest-even add, or an exact int32 add).
+ *
+ *   dtype      A, B elements         C and D elements    accumulation
+ *   GEMM_F16   IEEE binary16         float (fp32)        fp32 (MFMA)
+ *   GEMM_BF16  bfloat16              float (fp32)        fp32 (MFMA)
+ *   GEMM_I8    int8 (signed)         int32               int32 (MFMA), exact
+ *
+ * int8 results are exact whenever the true result fits in int32 (the
+ * accumulation wraps modulo 2^32, which is associative, so partial sums may
+ * overflow as long as the final value fits).  fp16/bf16 results satisfy, per
+ * element, |D - D_exact| <= 4*K*2^-24 * sum_k |a_ik b_kj| + 2^-24 * |c_ij|.
+ *
+ * Memory layout (element strides, not bytes):
+ *   A row-major (default):        A[i][k] at A[i*lda + k], lda >= K
+ *   A col-major (GEMM_A_COLMAJOR): A[i][k] at A[i + k*lda], lda >= M
+ *   B row-major (default):        B[k][j] at B[k*ldb + j], ldb >= N
+ *   B col-major (GEMM_B_COLMAJOR): B[k][j] at B[k + j*ldb], ldb >= K
+ *   C and D are row-major and share ldc >= N: X[i][j] at X[i*ldc + j]
+ *   Batches are contiguous: A_b = A + b*(row-major ? M : K)*lda,
+ *   B_b = B + b*(row-major ? K : N)*ldb, C_b = C + b*M*ldc, D_b = D + b*M*ldc.
+ *
+ * Ownership: the caller allocates A, B, C and D in device memory and keeps them
+ * alive until the work on `stream` has finished.  The library never frees caller
+ * memory.  A handle owns only a lazily grown device workspace (used by the
+ * split-K path) and cached device properties; one handle serves one host thread
+ * at a time.  D may alias C exactly (same pointer, same ldc); any other overlap
+ * between D and an input is undefined.
+ *
+ * Errors: every call returns a gemm_status_t.  Arguments are validated before
+ * anything is enqueued; on error nothing is launched.  Launches are
+ * asynchronous on `stream` (a hipStream_t, NULL = the null stream), so faults
+ * during execution surface at the caller's next synchronisation.
+ */
+#ifndef DMP_GEMM_H
+#define DMP_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_handle *gemm_handle_t;
+
+typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_I8 = 2 } gemm_dtype_t;
+
+/* flags: bitwise OR; default (0) is row-major A and row-major B. */
+enum { GEMM_A_COLMAJOR = 1u, GEMM_B_COLMAJOR = 2u };
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad dtype/flags */
+    GEMM_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950; there is no fallback */
+    GEMM_ERR_ALLOC = 3,              /* workspace allocation failed */
+    GEMM_ERR_HIP = 4                 /* a HIP API call or kernel launch reported an error */
+} gemm_status_t;
+
+/*
+ * Create a handle bound to the current HIP device.  *out receives the handle
+ * (NULL on failure).  Fails with GEMM_ERR_UNSUPPORTED_DEVICE unless the device
+ * is gfx950.
+ */
+int gemm_create(gemm_handle_t *out);
+
+/*
+ * Enqueue D_b = A_b*B_b + C_b for b < batch on `stream` (layouts above).
+ * A, B, C, D: device pointers (must be non-NULL when the product is non-empty).
+ * M, N, K, batch >= 0.  M, N or batch == 0 is a no-op returning GEMM_OK.
+ * K == 0 gives D = C (A, B and their leading dimensions are then not used).
+ * dtype: a gemm_dtype_t.  flags: GEMM_A_COLMAJOR |
+ * GEMM_B_COLMAJOR.  Any pointer alignment and leading dimension is accepted;
+ * 16-byte aligned pointers with leading dimensions that are multiples of 16
+ * bytes take the fast tiled path.
+ */
+int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D,
+             int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+             int dtype, unsigned flags, int64_t batch, void *stream);
+
+/* Release the handle's workspace (after synchronising its device) and the handle. */
+int gemm_destroy(gemm_handle_t h);
+
+/* Static, human-readable name of a status code. */
+const char *gemm_status_string(int status);
+
+/*
+ * Describe, without launching anything, which kernel path gemm_run would take
+ * for these arguments: writes a NUL-terminated label of at most label_len bytes
+ * (e.g. "tile256x256 bf16 a:row b:col splitk=1 grid=256").  Validates
+ * the same way gemm_run does, except that no data pointers are needed and
+ * pointer alignment is assumed to be 16 bytes.  h may be NULL: the plan is then
+ * made for a 256-CU gfx950 without any HIP call (host-only use).
+ */
+int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+              int64_t ldc, int dtype, unsigned flags, int64_t batch, char *label,
+              size_t label_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMP_GEMM_H */

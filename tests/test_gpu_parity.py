@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Float paths are held to |D - D_ref| <= 4*K*2^-24*sum|a*b| + 2^-24*|c| per element;
+int8 and exact-integer float inputs must match bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (DTYPE_CODE, check_full, check_points, check_row_sums, log, run, sample_points,
+                      to_device)
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_mixed_precision_02_amd as dmp
+    h = dmp.Handle()
+    yield h
+    h.close()
+
+
+def gpu_result(handle, p, **kw):
+    D = run(handle, p, **kw)
+    torch.cuda.synchronize()
+    return D.cpu().numpy()
+
+
+# ------------------------------------------------------------------ workloads
+
+SAMPLES = {"C2": 3000, "C3": 3000, "C5": 600, "S1": 3000}
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "S1"])
+def test_workload_parity(handle, name):
+    import dense_mixed_precision_02_amd as dmp
+    p = synth.config_problem(name)
+    flags = (1 if p.a_col else 0) | (2 if p.b_col else 0)
+    lbl = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, DTYPE_CODE[p.dtype], flags, p.batch)
+    log(f"[parity] {name}: {synth.CONFIG_LABELS[name]} plan={lbl}")
+    D = gpu_result(handle, p)
+    if name in ("C1", "C4"):
+        r = check_full(p, D)
+    else:
+        r = check_points(p, D, sample_points(p, SAMPLES[name], seed=sum(map(ord, name))))
+    check_row_sums(p, D)
+    log(f"[parity] {name}: ok, max err/bound {r:.3g}")
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "S1"])
+def test_workload_exact_integer_inputs(handle, name):
+    """A, B in {-1, 0, 1} and small-integer C at each workload's shape: every partial sum is
+    an integer below 2^24 in magnitude, so the result must equal the oracle exactly."""
+    p = synth.exact_variant(name)
+    log(f"[exact] {name}")
+    D = gpu_result(handle, p)
+    if name in ("C1", "C4"):
+        check_full(p, D, exact=True)
+    else:
+        check_points(p, D, sample_points(p, 800 if name != "C5" else 300, seed=5), exact=True)
+    check_row_sums(p, D, exact=True)
+
+
+# ------------------------------------------------------------ shapes / layouts
+
+SHAPES = [(1, 1, 8), (7, 9, 16), (33, 65, 24), (64, 64, 64), (130, 67, 136), (257, 263, 200),
+          (300, 520, 1040), (520, 300, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("a_col,b_col", [(False, False), (False, True), (True, False), (True, True)])
+def test_ragged_shapes_all_layouts(handle, dtype, a_col, b_col):
+    for n, (M, N, K) in enumerate(SHAPES):
+        if dtype == "i8" and K % 16:
+            K = (K // 16 + 1) * 16
+        for pad in (0, 8):
+            p = synth.make_problem(dtype, M, N, K, a_col=a_col, b_col=b_col, pad=pad, seed=100 + n,
+                                   c_range=(-1.0, 1.0) if dtype != "i8" else (-1000, 1000))
+            log(f"[ragged] {dtype} a_col={a_col} b_col={b_col} {M}x{N}x{K} pad={pad}")
+            check_full(p, gpu_result(handle, p))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_generic_path_odd_k_and_unaligned(handle, dtype):
+    """K not a multiple of the 16-byte granule, odd leading dimensions, and operands at
+    an address that is not 16-byte aligned all go through the element-wise kernel."""
+    import dense_mixed_precision_02_amd as dmp
+    for (M, N, K, pad) in [(5, 7, 3, 0), (70, 33, 61, 1), (129, 130, 77, 3)]:
+        for a_col, b_col in [(False, False), (True, True), (False, True)]:
+            p = synth.make_problem(dtype, M, N, K, a_col=a_col, b_col=b_col, pad=pad, seed=7,
+                                   c_range=(-1.0, 1.0) if dtype != "i8" else (-99, 99))
+            log(f"[generic] {dtype} {M}x{N}x{K} pad={pad} a_col={a_col} b_col={b_col}")
+            check_full(p, gpu_result(handle, p))
+    # misaligned base pointers (shift by one element) on an otherwise aligned problem
+    p = synth.make_problem(dtype, 96, 96, 128, seed=9,
+                           c_range=(-1.0, 1.0) if dtype != "i8" else (-99, 99))
+    A, B, C = to_device(p)
+    A2 = torch.empty(A.numel() + 1, dtype=A.dtype, device=A.device)
+    A2[1:] = A.reshape(-1)
+    B2 = torch.empty(B.numel() + 1, dtype=B.dtype, device=B.device)
+    B2[1:] = B.reshape(-1)
+    D = torch.empty_like(C)
+    handle.run(A2.data_ptr() + A.element_size(), B2.data_ptr() + B.element_size(), C.data_ptr(),
+               D.data_ptr(), p.M, p.N, p.K, p.lda, p.ldb, p.ldc,
+               {"f16": 0, "bf16": 1, "i8": 2}[dtype], 0, 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check_full(p, D.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_split_k(handle, dtype):
+    """Small M x N with long K takes the split-K path (fixed-order reduction, C added once)."""
+    import dense_mixed_precision_02_amd as dmp
+    for (M, N, K) in [(128, 128, 8192), (200, 96, 16384), (256, 512, 4096 + 128)]:
+        p = synth.make_problem(dtype, M, N, K, seed=11,
+                               c_range=(-1.0, 1.0) if dtype != "i8" else (-(1 << 20), 1 << 20))
+        lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, {"bf16": 1, "i8": 2}[dtype])
+        log(f"[splitk] {dtype} {M}x{N}x{K} {lbl}")
+        assert "splitk=1 " not in lbl
+        check_full(p, gpu_result(handle, p))
+        e = synth.make_problem(dtype, M, N, K, seed=12, ab_dist="small_int",
+                               c_dist="small_int" if dtype != "i8" else "uniform_int",
+                               c_range=(-8, 8))
+        check_full(e, gpu_result(handle, e), exact=True)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_batched(handle, dtype):
+    for (M, N, K, batch, pad) in [(64, 64, 64, 512, 0), (17, 40, 48, 5, 0), (64, 64, 256, 3, 8),
+                                  (100, 70, 96, 4, 0)]:
+        p = synth.make_problem(dtype, M, N, K, batch=batch, pad=pad, seed=13,
+                               c_range=(-1.0, 1.0) if dtype != "i8" else (-999, 999))
+        log(f"[batched] {dtype} {batch} x {M}x{N}x{K} pad={pad}")
+        check_full(p, gpu_result(handle, p))
+
+
+# ------------------------------------------------------------ semantics / edges
+
+def test_d_aliases_c(handle):
+    p = synth.make_problem("bf16", 300, 260, 192, seed=21)
+    A, B, C = to_device(p)
+    run(handle, p, tensors=(A, B, C), D=C)
+    torch.cuda.synchronize()
+    check_full(p, C.cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_k_zero_copies_c(handle, dtype):
+    p = synth.make_problem(dtype, 33, 45, 0, batch=2, seed=22,
+                           c_range=(-1.0, 1.0) if dtype != "i8" else (-9, 9))
+    A, B, C = to_device(p)
+    D = torch.full_like(C, 7)
+    run(handle, p, tensors=(A, B, C), D=D)
+    torch.cuda.synchronize()
+    assert torch.equal(D, C)
+
+
+def test_empty_is_noop(handle):
+    C = torch.ones(4, 4, device="cuda")
+    D = torch.full_like(C, 5.0)
+    for (M, N, batch) in [(0, 4, 1), (4, 0, 1), (4, 4, 0)]:
+        handle.run(0, 0, C.data_ptr(), D.data_ptr(), M, N, 4, 4, 4, 4, 0, 0, batch, 0)
+    torch.cuda.synchronize()
+    assert torch.all(D == 5.0)
+
+
+def test_invalid_arguments_enqueue_nothing(handle):
+    C = torch.ones(8, 8, device="cuda")
+    D = torch.full_like(C, 3.0)
+    A = torch.zeros(8, 8, dtype=torch.int16, device="cuda")
+    bad = [
+        dict(M=-1), dict(K=-1), dict(lda=7), dict(ldb=7), dict(ldc=7), dict(dtype=5),
+        dict(flags=8), dict(batch=-1), dict(Aptr=0), dict(Cptr=0), dict(Dptr=0),
+        dict(Cptr=C.data_ptr() + 2),
+    ]
+    for b in bad:
+        args = dict(Aptr=A.data_ptr(), Bptr=A.data_ptr(), Cptr=C.data_ptr(), Dptr=D.data_ptr(),
+                    M=8, N=8, K=8, lda=8, ldb=8, ldc=8, dtype=0, flags=0, batch=1)
+        args.update(b)
+        rc = handle.status(args["Aptr"], args["Bptr"], args["Cptr"], args["Dptr"], args["M"],
+                           args["N"], args["K"], args["lda"], args["ldb"], args["ldc"],
+                           args["dtype"], args["flags"], args["batch"], 0)
+        assert rc == 1, b
+    torch.cuda.synchronize()
+    assert torch.all(D == 3.0)
+
+
+def test_run_to_run_bit_identical(handle):
+    for p in [synth.make_problem("bf16", 1024, 1024, 4096, b_col=True, seed=31, ab_dist="normal",
+                                 c_dist="zeros"),
+              synth.make_problem("bf16", 256, 256, 32768, seed=32),
+              synth.make_problem("i8", 512, 384, 2048, seed=33)]:
+        T = to_device(p)
+        D1 = run(handle, p, tensors=T).clone()
+        D2 = run(handle, p, tensors=T)
+        torch.cuda.synchronize()
+        assert torch.equal(D1, D2)
+
+
+def test_nondefault_stream(handle):
+    p = synth.make_problem("f16", 260, 300, 320, b_col=True, seed=41)
+    T = to_device(p)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        D = run(handle, p, tensors=T, stream=s)
+    s.synchronize()
+    check_full(p, D.cpu().numpy())
+
+
+def test_torch_front_end(handle):
+    """dmp.gemm on torch tensors: layouts are read from strides, out= may be C."""
+    import dense_mixed_precision_02_amd as dmp
+    g = torch.Generator(device="cpu").manual_seed(5)
+    A = (torch.rand(200, 136, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    Bt = (torch.rand(96, 136, generator=g) * 2 - 1).to(torch.bfloat16).cuda()
+    C = (torch.rand(200, 96, generator=g) * 2 - 1).cuda()
+    D = dmp.gemm(A, Bt.t(), C)
+    ref = A.double().cpu() @ Bt.double().cpu().t() + C.double().cpu()
+    sabs = A.double().abs().cpu() @ Bt.double().abs().cpu().t()
+    tol = 4 * 136 * 2.0 ** -24 * sabs + 2.0 ** -24 * C.double().abs().cpu()
+    torch.cuda.synchronize()
+    assert torch.all((D.double().cpu() - ref).abs() <= tol)
+    A8 = torch.randint(-128, 128, (3, 64, 128), dtype=torch.int8, generator=g).cuda()
+    B8 = torch.randint(-128, 128, (3, 128, 32), dtype=torch.int8, generator=g).cuda()
+    C8 = torch.randint(-1000, 1000, (3, 64, 32), dtype=torch.int32, generator=g).cuda()
+    ref8 = torch.bmm(A8.cpu().long(), B8.cpu().long()) + C8.cpu().long()
+    D8 = dmp.gemm(A8, B8, C8, out=C8)
+    torch.cuda.synchronize()
+    assert torch.equal(D8.cpu().long(), ref8)
