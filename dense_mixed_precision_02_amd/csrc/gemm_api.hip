@@ -55,7 +55,8 @@ int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const
     if (K > 0 && ldb < std::max<int64_t>(1, b_col ? K : N)) return GEMM_ERR_INVALID_ARG;
     if (ldc < std::max<int64_t>(1, N)) return GEMM_ERR_INVALID_ARG;
     // grid dimensions and element indices are kept well inside their integer types
-    if (M > (1ll << 31) - 1024 || N > (1ll << 31) - 1024 || batch > (1ll << 30))
+    if (M > (1ll << 31) - 1024 || N > (1ll << 31) - 1024 || K > (1ll << 31) - 1024 ||
+        batch > (1ll << 30))
         return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     if (!check_ptrs) return GEMM_OK;

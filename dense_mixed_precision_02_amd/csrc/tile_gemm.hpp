@@ -27,6 +27,8 @@
 //    consecutive k values of its own row -- the K-contiguous register layout the
 //    MFMA needs.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace dmp {
@@ -94,19 +96,20 @@ struct Operand {
     }
     static constexpr int KSTEP = KB * (8 * NW) / (R / 16);  // MN-contig: k-rows between chunks
 
-    // Issue this wave's share of the copy of one k-tile into LDS buffer `lds`.
-    // base: element (row0, k0) of the operand.  kleft: valid k elements from k0.
-    __device__ void issue(const void *base, DMP_LDS char *lds, int wave, int kleft, int64_t Rtot) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-            const int c = j * NW + wave;
-            bool ok;
-            if (KCONTIG) ok = (row_or_k + 8 * NW * j < Rtot) && (fixed < kleft);
-            else ok = (fixed < Rtot) && (row_or_k + KSTEP * j < kleft);
-            load_granule_to_lds(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
-        }
+    // Issue chunk j of this wave's share of the copy of one k-tile into LDS
+    // buffer `lds`.  rs: buffer over element (row0, k0) of the operand.
+    // kleft: valid k elements from k0.
+    __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
+                          int kleft, int64_t Rtot) const {
+        const int c = j * NW + wave;
+        bool ok;
+        if (KCONTIG) ok = (row_or_k + 8 * NW * j < Rtot) && (fixed < kleft);
+        else ok = (fixed < Rtot) && (row_or_k + KSTEP * j < kleft);
+        load_granule_to_lds(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
     }
+
+    // LDS reads one fragment takes
+    static constexpr int READS = KCONTIG ? 1 : 2;
 
     // 16-byte fragment for MFMA step s (2 granules of K) of rows [rbase, rbase+32):
     // lane L gets row rbase + L%32 and K granule 2s + L/32 of the k-tile.
@@ -151,6 +154,20 @@ struct Operand {
     }
 };
 
+// Scheduling hint for one MFMA step: NM MFMAs with ND LDS reads and NV global
+// loads spread evenly between them (each read or load sits behind an MFMA).
+template <int NM, int ND, int NV, int I = 0>
+__device__ static inline void interleave() {
+    if constexpr (I < NM) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        constexpr int nd = ND * (I + 1) / NM - ND * I / NM;
+        constexpr int nv = NV * (I + 1) / NM - NV * I / NM;
+        if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);  // LDS reads
+        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // global loads
+        interleave<NM, ND, NV, I + 1>();
+    }
+}
+
 // The two LDS buffers are distinct arrays so that the compiler can tell that
 // copies into one never alias fragment reads from the other.
 template <class DT, int BM, int BN, int WM, int WN, bool AK, bool BKC>
@@ -191,7 +208,8 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int64_t k_begin = (int64_t)split * p.k_chunk;
     const int64_t k_end = min(p.K, k_begin + p.k_chunk);
-    const int nkt = k_end > k_begin ? (int)((k_end - k_begin + KT - 1) / KT) : 0;
+    const int kspan = k_end > k_begin ? (int)(k_end - k_begin) : 0;  // K < 2^31
+    const int nkt = (kspan + KT - 1) / KT;
 
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
@@ -214,12 +232,32 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     // (every granule out of range), so the loop below has a single exit.
     const int ntiles = nkt + (nkt & 1);
     const int64_t k_first = k_begin - (int64_t)(nkt & 1) * KT;
-    auto stage = [&](int kt, DMP_LDS char *la, DMP_LDS char *lb) {
+    // The copy of one k-tile is NCH wave-wide loads per wave (A chunks, then B
+    // chunks), issued in three parts spread over three MFMA steps so that the
+    // wave never blocks on a full load queue with MFMAs waiting behind it.
+    constexpr int NCH = OpA::CPW + OpB::CPW;
+    constexpr int P1 = (NCH + 2) / 3, P2 = P1 + (NCH - P1 + 1) / 2;
+    auto stage_part = [&](int kt, DMP_LDS char *la, DMP_LDS char *lb, auto lo_c, auto hi_c) {
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+        // k-tiles outside [k_begin, k_end) (the padding tile, and the ones past
+        // the end that the loop below still issues) load zeros and touch no memory
         const int64_t k0 = k_first + (int64_t)kt * KT;
-        const int kleft = k0 < k_begin ? 0 : (int)min<int64_t>(k_end - k0, KT);
-        opa.issue(OpA::tile_base(Ab, p.lda, m0, k0), la, wave, kleft, p.M);
-        opb.issue(OpB::tile_base(Bb, p.ldb, n0, k0), lb, wave, kleft, p.N);
+        const int koff = (kt - (nkt & 1)) * KT;  // k0 - k_begin
+        int kleft = kspan - koff;
+        kleft = kleft > KT ? KT : kleft;
+        kleft = ((koff < 0) | (kleft < 0)) ? 0 : kleft;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(OpA::tile_base(Ab, p.lda, m0, k0));
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(OpB::tile_base(Bb, p.ldb, n0, k0));
+#pragma unroll
+        for (int c = LO; c < HI; ++c) {
+            if (c < OpA::CPW) opa.issue(ra, la, wave, c, kleft, p.M);
+            else opb.issue(rb, lb, wave, c - OpA::CPW, kleft, p.N);
+        }
     };
+    using Z = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, P1>;
+    using I2 = std::integral_constant<int, P2>;
+    using I3 = std::integral_constant<int, NCH>;
     // Fragments for step s of the k-tile held in (la, lb).
     auto read = [&](intx4 (&fa)[TM], intx4 (&fb)[TN], const DMP_LDS char *la,
                     const DMP_LDS char *lb, int s) {
@@ -234,6 +272,8 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = DT::mfma(fa[i], fb[j], acc[i][j]);
     };
+    constexpr int NMF = TM * TN;                                   // MFMAs per step
+    constexpr int NRD = TM * OpA::READS + TN * OpB::READS;        // LDS reads per step
 
     DMP_LDS char *LA[2] = {(DMP_LDS char *)lds_a0, (DMP_LDS char *)lds_a1};
     DMP_LDS char *LB[2] = {(DMP_LDS char *)lds_b0, (DMP_LDS char *)lds_b1};
@@ -241,27 +281,46 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     // Software pipeline.  Fragments of step s+1 are read while the MFMAs of step
     // s run.  Before the last step of k-tile kt every wave waits for k-tile kt+1
     // to land and for its own reads of kt to finish; after that barrier the
-    // buffer of kt is free and receives k-tile kt+2, and step 0 of kt+1 is read
-    // from the other buffer while the MFMAs of step 3 of kt run.
+    // buffer of kt is free: the copy of k-tile kt+2 into it starts in step 3 of
+    // kt and finishes in steps 0 and 1 of kt+1, and step 0 of kt+1 is read from
+    // the other buffer while the MFMAs of step 3 of kt run.  Inside each step
+    // the LDS reads and loads are interleaved with the MFMAs; to keep each step
+    // one branch-free block they are issued even past the last k-tile, where
+    // they read nothing (zero-fill) or read a buffer no longer used.
     intx4 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     auto ktile = [&](int kt, int cur) {
-        read(fa1, fb1, LA[cur], LB[cur], 1);
+        DMP_LDS char *la = LA[cur], *lb = LB[cur], *na = LA[cur ^ 1], *nb = LB[cur ^ 1];
+        // step 0
+        read(fa1, fb1, la, lb, 1);
+        stage_part(kt + 1, na, nb, I1{}, I2{});
         mma(fa0, fb0);
-        read(fa0, fb0, LA[cur], LB[cur], 2);
+        interleave<NMF, NRD, P2 - P1>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 1
+        read(fa0, fb0, la, lb, 2);
+        stage_part(kt + 1, na, nb, I2{}, I3{});
         mma(fa1, fb1);
-        read(fa1, fb1, LA[cur], LB[cur], 3);
+        interleave<NMF, NRD, NCH - P2>();
+        __builtin_amdgcn_sched_barrier(0);
+        // step 2
+        read(fa1, fb1, la, lb, 3);
         mma(fa0, fb0);
+        interleave<NMF, NRD, 0>();
+        __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();
         __syncthreads();
-        if (kt + 2 < ntiles) stage(kt + 2, LA[cur], LB[cur]);
-        if (kt + 1 < ntiles) read(fa0, fb0, LA[cur ^ 1], LB[cur ^ 1], 0);
+        // step 3
+        stage_part(kt + 2, la, lb, Z{}, I1{});
+        read(fa0, fb0, na, nb, 0);
         mma(fa1, fb1);
+        interleave<NMF, NRD, P1>();
+        __builtin_amdgcn_sched_barrier(0);
     };
     if (nkt > 0) {
-        stage(0, LA[0], LB[0]);
+        stage_part(0, LA[0], LB[0], Z{}, I3{});
         wait_vmcnt<0>();
         __syncthreads();
-        if (ntiles > 1) stage(1, LA[1], LB[1]);
+        stage_part(1, LA[1], LB[1], Z{}, I1{});
         read(fa0, fb0, LA[0], LB[0], 0);
         // two k-tiles per trip so that each buffer is named statically
         for (int kt = 0; kt < ntiles; kt += 2) {
@@ -272,41 +331,83 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
 
     // ---- epilogue -----------------------------------------------------------
     // Accumulator register G of lane L in a 32x32 tile holds row
-    // 8*(G/4) + 4*(L/32) + G%4 and column L%32.
-    const int64_t rbase = m0 + wm * WTM + 4 * (lane >> 5);
-    const int64_t cbase = n0 + wn * WTN + (lane & 31);
-    if (p.partial) {
-        acc_t *Wb = (acc_t *)p.W + ((int64_t)split * p.batch + b) * p.M * p.N;
+    // 8*(G/4) + 4*(L/32) + G%4 and column L%32: a lane's values are scattered
+    // over rows.  Each wave therefore passes its tile through LDS one 32-row
+    // slab at a time and leaves it row-major, so that C is read and D written
+    // as 16-byte vectors covering whole row segments.
+    wait_vmcnt<0>();  // the zero-fill loads issued past the last k-tile have landed
+    __syncthreads();  // every wave is done with the operand buffers
+    DMP_LDS char *slab_c = wave == 0 ? LA[0] : wave == 1 ? LB[0] : wave == 2 ? LA[1] : LB[1];
+    DMP_LDS acc_t *slab = (DMP_LDS acc_t *)slab_c;
+    constexpr int SP = WTN + 8;        // padded slab row (elements): rows r and r+4 land 128 B apart mod 256
+    static_assert(32 * SP * 4 <= OpA::BYTES && 32 * SP * 4 <= OpB::BYTES, "slab must fit");
+    constexpr int LPR = WTN / 4;       // lanes per slab row (4 elements each)
+    constexpr int RPP = 64 / LPR;      // slab rows per pass
+    constexpr int PASSES = 32 / RPP;
+    const int64_t col_w = n0 + wn * WTN;
+    acc_t *Wb = p.partial ? (acc_t *)p.W + ((int64_t)split * p.batch + b) * p.M * p.N : nullptr;
+    const acc_t *Cb = (const acc_t *)p.C + (int64_t)b * p.sC;
+    acc_t *Db = (acc_t *)p.D + (int64_t)b * p.sC;
+    // 16-byte C/D accesses need 4-element alignment of every row start
+    const int64_t ldo = p.partial ? p.N : p.ldc;
+    const bool vec_ok = (ldo % 4 == 0) &&
+                        (p.partial ? ((uintptr_t)Wb % 16 == 0)
+                                   : ((uintptr_t)Cb % 16 == 0 && (uintptr_t)Db % 16 == 0));
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+        // accumulators of rows [i*32, i*32+32) of the wave tile -> LDS, row-major
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t col = cbase + j * 32;
-                if (col >= p.N) continue;
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int G = 0; G < 16; ++G) {
-                    const int64_t row = rbase + i * 32 + 8 * (G >> 2) + (G & 3);
-                    if (row < p.M) Wb[row * p.N + col] = acc[i][j][G];
+            for (int G = 0; G < 16; ++G)
+                slab[(8 * (G >> 2) + 4 * (lane >> 5) + (G & 3)) * SP + j * 32 + (lane & 31)] =
+                    acc[i][j][G];
+        // LDS instructions of one wave complete in order; this only keeps the
+        // compiler from moving the reads above the writes
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const int64_t row_s = m0 + wm * WTM + i * 32;
+        typedef acc_t vec4 __attribute__((ext_vector_type(4)));
+        vec4 cv[PASSES];
+        // issue every C load of the slab before using any
+        if (!p.partial) {
+#pragma unroll
+            for (int q = 0; q < PASSES; ++q) {
+                const int r = q * RPP + lane / LPR;
+                const int64_t grow = row_s + r, gcol = col_w + (lane % LPR) * 4;
+                const int64_t idx = grow * ldo + gcol;
+                if (vec_ok && grow < p.M && gcol + 3 < p.N) {
+                    cv[q] = *(const vec4 *)(Cb + idx);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        cv[q][e] = (grow < p.M && gcol + e < p.N) ? Cb[idx + e] : acc_t(0);
                 }
             }
-    } else {
-        const acc_t *Cb = (const acc_t *)p.C + (int64_t)b * p.sC;
-        acc_t *Db = (acc_t *)p.D + (int64_t)b * p.sC;
+        }
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int q = 0; q < PASSES; ++q) {
+            const int r = q * RPP + lane / LPR;
+            const int cl = (lane % LPR) * 4;
+            const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+            const int64_t grow = row_s + r, gcol = col_w + cl;
+            const int64_t idx = grow * ldo + gcol;
+            vec4 o;
+            if (p.partial) {
+                o = v;
+            } else {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int64_t col = cbase + j * 32;
-                if (col >= p.N) continue;
-#pragma unroll
-                for (int G = 0; G < 16; ++G) {
-                    const int64_t row = rbase + i * 32 + 8 * (G >> 2) + (G & 3);
-                    if (row < p.M) {
-                        const int64_t idx = row * p.ldc + col;
-                        Db[idx] = add_acc(acc[i][j][G], Cb[idx]);
-                    }
-                }
+                for (int e = 0; e < 4; ++e) o[e] = add_acc(v[e], cv[q][e]);
             }
+            acc_t *dst = p.partial ? Wb : Db;
+            if (vec_ok && grow < p.M && gcol + 3 < p.N) {
+                *(vec4 *)(dst + idx) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (grow < p.M && gcol + e < p.N) dst[idx + e] = o[e];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
 }
 
