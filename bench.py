@@ -31,6 +31,9 @@ DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2}
 # intensity below the ~315 FLOP/byte ridge).
 HBM_BOUND = {"C4"}
 METRIC = "GEMM TFLOPS/TOPS (fp16, bf16, int8) on 1 MI355X; % of dense MFMA peak"
+COPY_BYTES = 512 << 20
+# rocprofv3 HBM-traffic summary of the dominant kernel of each workload
+TRAFFIC_FILES = {"C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md"}
 
 
 def algorithmic_bytes(p) -> int:
@@ -109,6 +112,8 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of COPY_BYTES (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -119,8 +124,18 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_probe:
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(6):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 6}))
+        return
+
     import dense_mixed_precision_02_amd as dmp
     import synth
+    from bench_profile import kernel_source_hash, read_traffic
 
     name = args.config
     p = synth.config_problem(name)
@@ -169,6 +184,11 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": unit,
                 "frac": round(tflops / peak, 4), "traffic": None}
+    # measured HBM bytes per launch, only while the kernel sources are unchanged
+    tf = TRAFFIC_FILES.get(name)
+    rt = read_traffic(os.path.join(ROOT, tf)) if tf else None
+    if rt is not None and rt[1] == kernel_source_hash():
+        roof["traffic"] = round(rt[0])
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),

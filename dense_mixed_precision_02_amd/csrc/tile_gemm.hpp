@@ -233,10 +233,11 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     const int ntiles = nkt + (nkt & 1);
     const int64_t k_first = k_begin - (int64_t)(nkt & 1) * KT;
     // The copy of one k-tile is NCH wave-wide loads per wave (A chunks, then B
-    // chunks), issued in three parts spread over three MFMA steps so that the
-    // wave never blocks on a full load queue with MFMAs waiting behind it.
+    // chunks), issued in two parts spread over two MFMA steps so that the wave
+    // never blocks on a full load queue with MFMAs waiting behind it, and each
+    // part still has two steps to land before the next barrier.
     constexpr int NCH = OpA::CPW + OpB::CPW;
-    constexpr int P1 = (NCH + 2) / 3, P2 = P1 + (NCH - P1 + 1) / 2;
+    constexpr int P1 = (NCH + 1) / 2, P2 = NCH;
     auto stage_part = [&](int kt, DMP_LDS char *la, DMP_LDS char *lb, auto lo_c, auto hi_c) {
         constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
         // k-tiles outside [k_begin, k_end) (the padding tile, and the ones past
@@ -257,7 +258,6 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     using Z = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, P1>;
     using I2 = std::integral_constant<int, P2>;
-    using I3 = std::integral_constant<int, NCH>;
     // Fragments for step s of the k-tile held in (la, lb).
     auto read = [&](intx4 (&fa)[TM], intx4 (&fb)[TN], const DMP_LDS char *la,
                     const DMP_LDS char *lb, int s) {
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     // s run.  Before the last step of k-tile kt every wave waits for k-tile kt+1
     // to land and for its own reads of kt to finish; after that barrier the
     // buffer of kt is free: the copy of k-tile kt+2 into it starts in step 3 of
-    // kt and finishes in steps 0 and 1 of kt+1, and step 0 of kt+1 is read from
+    // kt and finishes in step 0 of kt+1, and step 0 of kt+1 is read from
     // the other buffer while the MFMAs of step 3 of kt run.  Inside each step
     // the LDS reads and loads are interleaved with the MFMAs; to keep each step
     // one branch-free block they are issued even past the last k-tile, where
@@ -298,9 +298,8 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         // step 1
         read(fa0, fb0, la, lb, 2);
-        stage_part(kt + 1, na, nb, I2{}, I3{});
         mma(fa1, fb1);
-        interleave<NMF, NRD, NCH - P2>();
+        interleave<NMF, NRD, 0>();
         __builtin_amdgcn_sched_barrier(0);
         // step 2
         read(fa1, fb1, la, lb, 3);
@@ -317,7 +316,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
     if (nkt > 0) {
-        stage_part(0, LA[0], LB[0], Z{}, I3{});
+        stage_part(0, LA[0], LB[0], Z{}, I2{});
         wait_vmcnt<0>();
         __syncthreads();
         stage_part(1, LA[1], LB[1], Z{}, I1{});
