@@ -74,24 +74,45 @@ __global__ __launch_bounds__(64) void generic_gemm(const GenericArgs p) {
 // Split-K reduction: D = (P_0 + P_1 + ... + P_{S-1}) + C, summed in that fixed
 // order (so the result is the same on every run), with C added once at the end.
 // With S == 0 it copies C to D.  W holds S*batch dense M x N partial tiles.
-template <class T>
+// VEC: each thread handles 4 consecutive elements of a row with 16-byte
+// accesses (N and ldc multiples of 4, 16-byte aligned C, D and W).
+template <class T, bool VEC>
 __global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, const T *C, T *D,
                                                      int64_t M, int64_t N, int64_t ldc, int64_t batch,
                                                      int S) {
+    constexpr int V = VEC ? 4 : 1;
+    typedef T vec __attribute__((ext_vector_type(4)));
     const int64_t MN = M * N;
     const int64_t total = MN * batch;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t groups = total / V;
+    for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e4 < groups;
+         e4 += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = e4 * V;
         const int64_t b = e / MN, rem = e - b * MN;
         const int64_t i = rem / N, j = rem - i * N;
         const int64_t idx = b * M * ldc + i * ldc + j;
-        if (S == 0) {
-            D[idx] = C[idx];
-            continue;
+        if constexpr (VEC) {
+            vec s = *(const vec *)(C + idx);
+            if (S > 0) {
+                vec acc = *(const vec *)(W + e);
+                for (int q = 1; q < S; ++q) {
+                    const vec w = *(const vec *)(W + (int64_t)q * total + e);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) acc[t] = add_acc(acc[t], w[t]);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) s[t] = add_acc(acc[t], s[t]);
+            }
+            *(vec *)(D + idx) = s;
+        } else {
+            if (S == 0) {
+                D[idx] = C[idx];
+                continue;
+            }
+            T acc = W[e];
+            for (int q = 1; q < S; ++q) acc = add_acc(acc, W[(int64_t)q * total + e]);
+            D[idx] = add_acc(acc, C[idx]);
         }
-        T s = W[e];
-        for (int q = 1; q < S; ++q) s = add_acc(s, W[(int64_t)q * total + e]);
-        D[idx] = add_acc(s, C[idx]);
     }
 }
 

@@ -191,8 +191,30 @@ hipError_t launch_cfg(int cfg, const TileArgs &a, bool a_col, bool b_col, int64_
     }
 }
 
-int64_t reduce_grid(int64_t elems) {
-    return std::max<int64_t>(1, std::min<int64_t>(cdiv(elems, 256), 256 * 64));
+int64_t reduce_grid(int64_t items) {
+    return std::max<int64_t>(1, std::min<int64_t>(cdiv(items, 256), 256 * 64));
+}
+
+template <class T>
+hipError_t launch_reduce_t(const void *W, const void *C, void *D, int64_t M, int64_t N, int64_t ldc,
+                           int64_t batch, int S, hipStream_t s) {
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 && aligned16(C) && aligned16(D) &&
+                     (S == 0 || aligned16(W));
+    const int64_t elems = M * N * batch;
+    if (vec)
+        hipLaunchKernelGGL((splitk_reduce<T, true>), dim3((unsigned)reduce_grid(elems / 4)), dim3(256), 0,
+                           s, (const T *)W, (const T *)C, (T *)D, M, N, ldc, batch, S);
+    else
+        hipLaunchKernelGGL((splitk_reduce<T, false>), dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
+                           (const T *)W, (const T *)C, (T *)D, M, N, ldc, batch, S);
+    return hipGetLastError();
+}
+
+// Fixed-order sum of S split-K partials plus C into D (S == 0: D = C).
+hipError_t launch_reduce(int dtype, const void *W, const void *C, void *D, int64_t M, int64_t N,
+                         int64_t ldc, int64_t batch, int S, hipStream_t s) {
+    if (dtype == GEMM_I8) return launch_reduce_t<int32_t>(W, C, D, M, N, ldc, batch, S, s);
+    return launch_reduce_t<float>(W, C, D, M, N, ldc, batch, S, s);
 }
 
 }  // namespace
@@ -277,16 +299,9 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
     const Plan P = make_plan(h, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
     if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
 
-    if (P.copy_only) {
-        const int64_t elems = M * N * batch;
-        if (dtype == GEMM_I8)
-            hipLaunchKernelGGL(splitk_reduce<int32_t>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0,
-                               s, nullptr, (const int32_t *)C, (int32_t *)D, M, N, ldc, batch, 0);
-        else
-            hipLaunchKernelGGL(splitk_reduce<float>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
-                               nullptr, (const float *)C, (float *)D, M, N, ldc, batch, 0);
-        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
-    }
+    if (P.copy_only)
+        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, s) == hipSuccess ? GEMM_OK
+                                                                                     : GEMM_ERR_HIP;
 
     if (P.cfg == CFG_GENERIC) {
         GenericArgs g;
@@ -336,18 +351,8 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
     else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_col, P.grid, s);
     else e = launch_cfg<I8>(P.cfg, t, a_col, b_col, P.grid, s);
     if (e != hipSuccess) return GEMM_ERR_HIP;
-    if (P.reduce) {
-        const int64_t elems = M * N * batch;
-        if (dtype == GEMM_I8)
-            hipLaunchKernelGGL(splitk_reduce<int32_t>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0,
-                               s, (const int32_t *)h->ws, (const int32_t *)C, (int32_t *)D, M, N, ldc,
-                               batch, P.splits);
-        else
-            hipLaunchKernelGGL(splitk_reduce<float>, dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
-                               (const float *)h->ws, (const float *)C, (float *)D, M, N, ldc, batch,
-                               P.splits);
-        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
-    }
+    if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, s) != hipSuccess)
+        return GEMM_ERR_HIP;
     return GEMM_OK;
 }
 
