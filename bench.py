@@ -9,7 +9,10 @@ already resident in HBM.  Prints ONE JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-cpu]
 
 --config picks another workload of the same family (C1, C3, C4, C5, S1) for the
-documentation tables; the graded line is the default one.
+documentation tables; the graded line is the default one.  --d-type / --c-type /
+--alpha / --beta time the scaled, converted output stage instead
+(D = cvt_D(alpha*A*B + beta*C) through gemm_run_ex; --c-type none means beta = 0
+and no C read).
 """
 from __future__ import annotations
 
@@ -36,9 +39,27 @@ COPY_BYTES = 512 << 20
 TRAFFIC_FILES = {"C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md"}
 
 
-def algorithmic_bytes(p) -> int:
+OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4, "none": 0}
+
+
+def algorithmic_bytes(p, c_type=None, d_type=None) -> int:
     """Compulsory HBM traffic of one call: A, B and C read once, D written once."""
-    return p.A.nbytes + p.B.nbytes + 2 * p.C.nbytes
+    elems = p.C.size
+    csz = p.C.itemsize if c_type is None else OUT_SIZE[c_type]
+    dsz = p.C.itemsize if d_type is None else OUT_SIZE[d_type]
+    return p.A.nbytes + p.B.nbytes + elems * (csz + dsz)
+
+
+def store_c(c_type, C):
+    """C values in the storage of c_type (input generation only)."""
+    import numpy as np
+
+    import synth
+    if c_type == "f16":
+        return synth.f64_to_f16_bits(C.astype(np.float64))
+    if c_type == "bf16":
+        return synth.f32_to_bf16_bits(C.astype(np.float32))
+    return C
 
 
 def cpu_baseline(p, budget_s: float = 15.0):
@@ -84,7 +105,7 @@ def cpu_baseline(p, budget_s: float = 15.0):
             "sample": f"{what} of the same seeded problem ({fl / 2:.3g} MACs, {dt:.1f} s)"}
 
 
-def parity_sample(p, D_host):
+def parity_sample(p, D_host, ex=None):
     """Oracle check of the benchmarked output at sampled positions (not timed)."""
     import numpy as np
 
@@ -94,6 +115,17 @@ def parity_sample(p, D_host):
     pts = np.stack([rng.integers(0, p.batch, n), rng.integers(0, p.M, n),
                     rng.integers(0, p.N, n)], 1).astype(np.int64)
     Dg = D_host.reshape(p.batch, p.M, p.ldc)[pts[:, 0], pts[:, 1], pts[:, 2]]
+    if ex is not None:
+        c_type, d_type, alpha, beta, Cst = ex
+        P, S = oracle.gemm_points(p.dtype, p.A, p.B, np.zeros_like(p.C), pts, **p.oracle_args())
+        if d_type != "f32":
+            Dg = oracle.decode_c(d_type, Dg.view(np.uint16))
+        c = (oracle.decode_c(c_type, Cst).reshape(p.batch, p.M, p.ldc)[pts[:, 0], pts[:, 1], pts[:, 2]]
+             if c_type != "none" else np.zeros(n))
+        Dref = oracle.scaled_reference(P, c, alpha, beta)
+        tol = oracle.scaled_tolerance(p.K, S, c, Dref, alpha, beta, d_type)
+        ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+        return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     r = oracle.gemm_points(p.dtype, p.A, p.B, p.C, pts, **p.oracle_args())
     if p.dtype == "i8":
         ok = bool(np.array_equal(Dg.astype(np.int64), r))
@@ -112,6 +144,11 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--d-type", choices=["f32", "f16", "bf16"], default=None,
+                    help="time gemm_run_ex with this D storage type")
+    ap.add_argument("--c-type", choices=["f32", "f16", "bf16", "none"], default="f32")
+    ap.add_argument("--alpha", type=float, default=1.0)
+    ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (counter calibration)")
     args = ap.parse_args()
@@ -146,19 +183,41 @@ def main():
         t = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x)
         return t.to(dev)
 
-    A, B, C = up(p.A), up(p.B), up(p.C)
-    D = torch.empty_like(C)
+    ex = None
+    A, B = up(p.A), up(p.B)
+    if args.d_type is not None:
+        if p.dtype == "i8":
+            raise SystemExit("--d-type applies to fp16/bf16 workloads")
+        beta = 0.0 if args.c_type == "none" else args.beta
+        Cst = store_c(args.c_type, p.C) if args.c_type != "none" else None
+        ex = (args.c_type, args.d_type, args.alpha, beta, Cst)
+        C = up(Cst) if Cst is not None else None
+        D = torch.empty(p.C.shape, dtype=torch.float32 if args.d_type == "f32" else torch.int16,
+                        device=dev)
+    else:
+        C = up(p.C)
+        D = torch.empty_like(C)
     h = dmp.Handle()
     flags = (dmp.GEMM_A_COLMAJOR if p.a_col else 0) | (dmp.GEMM_B_COLMAJOR if p.b_col else 0)
     code = DTYPE_CODE[p.dtype]
     label = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch, handle=h)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    args_run = (A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(), p.M, p.N, p.K, p.lda,
-                p.ldb, p.ldc, code, flags, p.batch, sp)
+    args_run = (A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, D.data_ptr(),
+                p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch)
+    if ex is None:
+        def step():
+            h.run(*args_run, sp)
+    else:
+        OUTC = {"f32": dmp.GEMM_OUT_F32, "f16": dmp.GEMM_OUT_F16, "bf16": dmp.GEMM_OUT_BF16,
+                "none": dmp.GEMM_OUT_F32}
+        kw = dict(alpha=ex[2], beta=ex[3], c_type=OUTC[ex[0]], d_type=OUTC[ex[1]], stream=sp)
+
+        def step():
+            h.run_ex(*args_run, **kw)
 
     for _ in range(args.warmup):
-        h.run(*args_run)
+        step()
     torch.cuda.synchronize()
     # events on the stream the kernels are launched on
     e0 = torch.cuda.Event(enable_timing=True)
@@ -166,7 +225,7 @@ def main():
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
-        h.run(*args_run)
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -177,8 +236,9 @@ def main():
 
     peak = PEAK_TFLOPS[p.dtype]
     unit = "TOP/s" if p.dtype == "i8" else "TFLOP/s"
+    nbytes = algorithmic_bytes(p, *(ex[:2] if ex else (None, None)))
     if name in HBM_BOUND:
-        gbs = algorithmic_bytes(p) / (ms * 1e-3) / 1e9
+        gbs = nbytes / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
     else:
@@ -186,7 +246,7 @@ def main():
                 "frac": round(tflops / peak, 4), "traffic": None}
     # measured HBM bytes per launch, only while the kernel sources are unchanged
     tf = TRAFFIC_FILES.get(name)
-    rt = read_traffic(os.path.join(ROOT, tf)) if tf else None
+    rt = read_traffic(os.path.join(ROOT, tf)) if tf and ex is None else None
     if rt is not None and rt[1] == kernel_source_hash():
         roof["traffic"] = round(rt[0])
     line = {
@@ -206,11 +266,14 @@ def main():
                    "batch": p.batch, "a_layout": "col" if p.a_col else "row",
                    "b_layout": "col" if p.b_col else "row", "plan": label,
                    "pct_of_dense_peak": round(100 * tflops / peak, 2),
-                   "hbm_gbs_algorithmic": round(algorithmic_bytes(p) / (ms * 1e-3) / 1e9, 1),
+                   "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
                    "timed_wall_s": round(wall, 3)},
         "roofline": roof,
-        "parity": parity_sample(p, D_host),
+        "parity": parity_sample(p, D_host, ex),
     }
+    if ex is not None:
+        line["config"]["output_stage"] = {"c_type": ex[0], "d_type": ex[1], "alpha": ex[2],
+                                          "beta": ex[3]}
     h.close()
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)

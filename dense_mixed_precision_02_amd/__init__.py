@@ -10,13 +10,15 @@ stream.  PyTorch is used for device memory and streams only.
     B = torch.randn(4096, 4096, device="cuda").bfloat16().t()   # column-major view
     C = torch.zeros(4096, 4096, device="cuda")
     D = dmp.gemm(A, B, C)           # D = A @ B + C, fp32 accumulate
+    E = dmp.gemm(A, B, None, alpha=0.5, out_dtype=torch.bfloat16)   # bf16 result
 """
 from __future__ import annotations
 
 from .binding import (GEMM_A_COLMAJOR, GEMM_B_COLMAJOR, GEMM_BF16, GEMM_F16, GEMM_I8,
-                      GemmError, Handle, default_handle, gemm, lib_path, load_library,
+                      GEMM_OUT_BF16, GEMM_OUT_F16, GEMM_OUT_F32, GEMM_OUT_I32, GemmError, Handle, default_handle, gemm, lib_path, load_library,
                       plan_label, status_string, EXPORTED_SYMBOLS)
 
 __all__ = ["GEMM_A_COLMAJOR", "GEMM_B_COLMAJOR", "GEMM_BF16", "GEMM_F16", "GEMM_I8",
+           "GEMM_OUT_BF16", "GEMM_OUT_F16", "GEMM_OUT_F32", "GEMM_OUT_I32",
            "GemmError", "Handle", "default_handle", "gemm", "lib_path", "load_library",
            "plan_label", "status_string", "EXPORTED_SYMBOLS"]

@@ -10,9 +10,11 @@ _LIB_NAME = "libdmp_gemm.so"
 
 GEMM_F16, GEMM_BF16, GEMM_I8 = 0, 1, 2
 GEMM_A_COLMAJOR, GEMM_B_COLMAJOR = 1, 2
+GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32 = 0, 1, 2, 3
 GEMM_OK = 0
 
-EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_destroy", "gemm_status_string", "gemm_plan")
+EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy",
+                    "gemm_status_string", "gemm_plan")
 
 _lib = None
 _lock = threading.Lock()
@@ -49,6 +51,10 @@ def load_library():
         lib.gemm_run.restype = ctypes.c_int
         lib.gemm_run.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                  ctypes.c_int, ctypes.c_uint, i64, vp]
+        lib.gemm_run_ex.restype = ctypes.c_int
+        lib.gemm_run_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                    ctypes.c_int, ctypes.c_uint, i64, ctypes.c_float,
+                                    ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
         lib.gemm_plan.restype = ctypes.c_int
         lib.gemm_plan.argtypes = [vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_uint,
                                   i64, ctypes.c_char_p, ctypes.c_size_t]
@@ -108,6 +114,19 @@ class Handle:
         return load_library().gemm_run(self.ptr, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags,
                                        batch, stream)
 
+    def status_ex(self, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags=0, batch=1,
+                  alpha=1.0, beta=1.0, c_type=GEMM_OUT_F32, d_type=GEMM_OUT_F32,
+                  stream=0) -> int:
+        """Raw-pointer call of gemm_run_ex; returns the status code."""
+        return load_library().gemm_run_ex(self.ptr, A, B, C, D, M, N, K, lda, ldb, ldc, dtype,
+                                          flags, batch, alpha, beta, c_type, d_type, stream)
+
+    def run_ex(self, *args, **kw) -> None:
+        """Like status_ex() but raises on a non-zero status."""
+        rc = self.status_ex(*args, **kw)
+        if rc != GEMM_OK:
+            raise GemmError(rc, "gemm_run_ex")
+
 
 _default = {}
 
@@ -132,46 +151,72 @@ def _operand_layout(X, rows: int, cols: int, name: str):
     raise ValueError(f"{name} must be row-major or column-major in its last two dims")
 
 
-def gemm(A, B, C, out=None, handle: Handle | None = None):
-    """D = A @ B + C on the current stream.
+def _out_code(dtype):
+    import torch
+    return {torch.float32: GEMM_OUT_F32, torch.float16: GEMM_OUT_F16,
+            torch.bfloat16: GEMM_OUT_BF16, torch.int32: GEMM_OUT_I32}.get(dtype)
+
+
+def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtype=None,
+         handle: Handle | None = None):
+    """D = alpha * (A @ B) + beta * C on the current stream.
 
     A: (..., M, K) float16 / bfloat16 / int8;  B: (..., K, N) same dtype (row-major, or a
-    transposed view = column-major);  C: (..., M, N) float32 (int32 for int8), row-major.
-    Leading batch dims (one at most) must be contiguous in the library's sense.  Returns D
-    (a new tensor unless ``out`` is given; ``out`` may be C itself)."""
+    transposed view = column-major);  C: (..., M, N) row-major, float32 / float16 / bfloat16
+    for float inputs, int32 for int8 (None means beta = 0).  D has ``out_dtype`` (default:
+    float32, int32 for int8), a new tensor with C's strides unless ``out`` is given (``out``
+    may be C itself when the dtypes agree).  Leading batch dims (one at most) must be
+    contiguous in the library's sense.  int8 takes alpha == 1 and beta in {0, 1} only."""
     import torch
     dt = {torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16, torch.int8: GEMM_I8}.get(A.dtype)
     if dt is None or B.dtype != A.dtype:
         raise TypeError("A and B must both be float16, bfloat16 or int8")
     acc = torch.int32 if dt == GEMM_I8 else torch.float32
-    if C.dtype != acc:
-        raise TypeError(f"C must be {acc}")
-    if not (A.is_cuda and B.is_cuda and C.is_cuda):
+    if A.dim() != B.dim() or A.dim() not in (2, 3):
+        raise ValueError("A and B must both be 2-D or both 3-D")
+    if not (A.is_cuda and B.is_cuda):
         raise ValueError("tensors must be on the GPU")
-    if A.dim() != B.dim() or A.dim() != C.dim() or A.dim() not in (2, 3):
-        raise ValueError("A, B, C must all be 2-D or all 3-D")
     M, K = A.shape[-2], A.shape[-1]
     N = B.shape[-1]
-    if B.shape[-2] != K or C.shape[-2] != M or C.shape[-1] != N:
-        raise ValueError("shape mismatch")
     batch = A.shape[0] if A.dim() == 3 else 1
+    if B.shape[-2] != K or (A.dim() == 3 and B.shape[0] != batch):
+        raise ValueError("shape mismatch between A and B")
+    if C is None:
+        beta = 0.0
+    else:
+        if not C.is_cuda or C.dim() != A.dim() or C.shape[-2:] != (M, N):
+            raise ValueError("C must be a GPU tensor of shape (..., M, N)")
+        if C.stride(-1) != 1:
+            raise ValueError("C must be row-major")
+    c_code = _out_code(C.dtype) if C is not None else (GEMM_OUT_I32 if dt == GEMM_I8 else GEMM_OUT_F32)
+    if c_code is None:
+        raise TypeError("C must be float32, float16, bfloat16 or int32")
+    d_dtype = out.dtype if out is not None else (out_dtype if out_dtype is not None else acc)
+    d_code = _out_code(d_dtype)
+    if d_code is None:
+        raise TypeError("out dtype must be float32, float16, bfloat16 or int32")
     a_col, lda = _operand_layout(A, M, K, "A")
     b_col, ldb = _operand_layout(B, K, N, "B")
-    if C.stride(-1) != 1:
-        raise ValueError("C must be row-major")
-    ldc = max(C.stride(-2), N, 1)
+    shape = (batch, M, N) if A.dim() == 3 else (M, N)
+    if C is not None:
+        ldc = max(C.stride(-2), N, 1)
+        strides = C.stride()
+    else:
+        ldc = max(N, 1)
+        strides = (M * ldc, ldc, 1) if A.dim() == 3 else (ldc, 1)
     if out is None:
-        out = torch.empty_strided(C.shape, C.stride(), dtype=acc, device=C.device)
-    if out.stride() != C.stride() or out.dtype != acc:
-        raise ValueError("out must have C's strides and dtype")
+        out = torch.empty_strided(shape, strides, dtype=d_dtype, device=A.device)
+    if tuple(out.shape) != shape or out.stride() != strides:
+        raise ValueError("out must have shape (..., M, N) and C's strides")
     if batch > 1:
         want_a = (K if a_col else M) * lda
         want_b = (N if b_col else K) * ldb
-        if A.stride(0) != want_a or B.stride(0) != want_b or C.stride(0) != M * ldc:
+        if A.stride(0) != want_a or B.stride(0) != want_b or out.stride(0) != M * ldc:
             raise ValueError("batched operands must have contiguous batch strides")
     flags = (GEMM_A_COLMAJOR if a_col else 0) | (GEMM_B_COLMAJOR if b_col else 0)
     h = handle if handle is not None else default_handle()
     stream = torch.cuda.current_stream(A.device).cuda_stream
-    h.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), out.data_ptr(), M, N, K, lda, ldb, ldc, dt,
-          flags, batch, stream)
+    h.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, out.data_ptr(),
+             M, N, K, lda, ldb, ldc, dt, flags, batch, alpha=float(alpha), beta=float(beta),
+             c_type=c_code, d_type=d_code, stream=stream)
     return out

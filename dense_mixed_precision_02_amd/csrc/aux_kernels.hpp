@@ -12,6 +12,7 @@ struct GenericArgs {
     int64_t a_rs, a_ks, b_ks, b_cs;  // element strides: A[i][k] = A[i*a_rs + k*a_ks], B[k][j] = B[k*b_ks + j*b_cs]
     int64_t ldc, sA, sB, sC;
     int tiles_m, tiles_n;
+    EpiParams ep;  // output stage: alpha, beta, C and D storage types
 };
 
 // Element loads for the any-alignment path (no vector loads, no alignment
@@ -59,60 +60,61 @@ __global__ __launch_bounds__(64) void generic_gemm(const GenericArgs p) {
         }
         acc = DT::mfma(fa, fb, acc);
     }
-    const acc_t *Cb = (const acc_t *)p.C + b * p.sC;
-    acc_t *Db = (acc_t *)p.D + b * p.sC;
+    const char *Cb = (const char *)p.C + b * p.sC * out_size(p.ep.c_type);
+    char *Db = (char *)p.D + b * p.sC * out_size(p.ep.d_type);
+    typedef acc_t vec4 __attribute__((ext_vector_type(4)));
     const int64_t c = n0 + (lane & 31);
     if (c < p.N) {
 #pragma unroll
         for (int G2 = 0; G2 < 16; ++G2) {
             const int64_t r = m0 + 8 * (G2 >> 2) + 4 * (lane >> 5) + (G2 & 3);
-            if (r < p.M) Db[r * p.ldc + c] = add_acc(acc[G2], Cb[r * p.ldc + c]);
+            if (r < p.M) {
+                const int64_t idx = r * p.ldc + c;
+                vec4 a = {acc[G2], 0, 0, 0};
+                const vec4 cv = p.ep.use_c ? load4<acc_t>(Cb, idx, p.ep.c_type, false, 1) : vec4{0, 0, 0, 0};
+                store4<acc_t>(Db, idx, finish4(a, cv, p.ep), p.ep.d_type, false, 1);
+            }
         }
     }
 }
 
-// Split-K reduction: D = (P_0 + P_1 + ... + P_{S-1}) + C, summed in that fixed
-// order (so the result is the same on every run), with C added once at the end.
-// With S == 0 it copies C to D.  W holds S*batch dense M x N partial tiles.
-// VEC: each thread handles 4 consecutive elements of a row with 16-byte
-// accesses (N and ldc multiples of 4, 16-byte aligned C, D and W).
+// Split-K reduction and output stage: D = out(P_0 + P_1 + ... + P_{S-1}, C),
+// the partials summed in that fixed order (so the result is the same on every
+// run) and the output stage (alpha, beta, C once, conversion) applied at the
+// end.  With S == 0 the sum is zero (K == 0).  W holds S*batch dense M x N
+// partial tiles.  VEC: each thread handles 4 consecutive elements of a row with
+// vector accesses (N and ldc multiples of 4, aligned C, D and W).
 template <class T, bool VEC>
-__global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, const T *C, T *D,
+__global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, const void *C, void *D,
                                                      int64_t M, int64_t N, int64_t ldc, int64_t batch,
-                                                     int S) {
-    constexpr int V = VEC ? 4 : 1;
+                                                     int S, EpiParams ep) {
     typedef T vec __attribute__((ext_vector_type(4)));
+    constexpr int V = VEC ? 4 : 1;
     const int64_t MN = M * N;
     const int64_t total = MN * batch;
     const int64_t groups = total / V;
-    for (int64_t e4 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e4 < groups;
-         e4 += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t e = e4 * V;
+    for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+         g += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = g * V;
         const int64_t b = e / MN, rem = e - b * MN;
         const int64_t i = rem / N, j = rem - i * N;
         const int64_t idx = b * M * ldc + i * ldc + j;
-        if constexpr (VEC) {
-            vec s = *(const vec *)(C + idx);
-            if (S > 0) {
-                vec acc = *(const vec *)(W + e);
+        vec acc = {0, 0, 0, 0};
+        if (S > 0) {
+            if constexpr (VEC) {
+                acc = *(const vec *)(W + e);
                 for (int q = 1; q < S; ++q) {
                     const vec w = *(const vec *)(W + (int64_t)q * total + e);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) acc[t] = add_acc(acc[t], w[t]);
                 }
-#pragma unroll
-                for (int t = 0; t < 4; ++t) s[t] = add_acc(acc[t], s[t]);
+            } else {
+                acc[0] = W[e];
+                for (int q = 1; q < S; ++q) acc[0] = add_acc(acc[0], W[(int64_t)q * total + e]);
             }
-            *(vec *)(D + idx) = s;
-        } else {
-            if (S == 0) {
-                D[idx] = C[idx];
-                continue;
-            }
-            T acc = W[e];
-            for (int q = 1; q < S; ++q) acc = add_acc(acc, W[(int64_t)q * total + e]);
-            D[idx] = add_acc(acc, C[idx]);
         }
+        const vec cv = ep.use_c ? load4<T>(C, idx, ep.c_type, VEC, V) : vec{0, 0, 0, 0};
+        store4<T>(D, idx, finish4(acc, cv, ep), ep.d_type, VEC, V);
     }
 }
 

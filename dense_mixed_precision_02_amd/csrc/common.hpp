@@ -69,9 +69,16 @@ struct I8 {
 constexpr int OOB_OFFSET = 0x7ffffff0;
 
 __device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
+    // The descriptor must sit in scalar registers.  base is wave-uniform by
+    // construction; reading it from the first lane says so to the compiler,
+    // which otherwise may compute it in vector registers and wrap every buffer
+    // load in a loop over distinct descriptor values.
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = (void *)(((uint64_t)hi << 32) | lo);
     // dword3 0x00020000: 32-bit data format, the gfx9-family raw-buffer setting
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, OOB_OFFSET,
-                                             0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, OOB_OFFSET, 0x00020000);
 }
 
 // 16-byte global -> LDS copy that bypasses registers.  The LDS destination of
@@ -95,6 +102,129 @@ __device__ static inline void wait_vmcnt() {
 __device__ static inline float add_acc(float a, float b) { return a + b; }
 __device__ static inline int32_t add_acc(int32_t a, int32_t b) {
     return (int32_t)((uint32_t)a + (uint32_t)b);
+}
+
+// ---------------------------------------------------------------------------
+// Output stage.  D = cvt_D(alpha * acc + beta * cvt_C(C)) with every step an
+// fp32 round-to-nearest-even operation (no fused multiply-add), C decoded
+// exactly from its storage type and the final conversion to D's storage type
+// rounding to nearest even.  alpha = beta = 1 with fp32 C and D is the plain
+// D = acc + C.  The int8 path only has D = acc + C (int32, wrapping) or D = acc.
+// ---------------------------------------------------------------------------
+enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3 };
+
+struct EpiParams {
+    float alpha, beta;
+    int c_type, d_type;
+    int use_c;  // beta != 0: C is read
+};
+
+__device__ static inline int out_size(int t) { return (t == OUT_F16 || t == OUT_BF16) ? 2 : 4; }
+
+typedef uint16_t ushortx4 __attribute__((ext_vector_type(4)));
+template <class T> using vec4_of = T __attribute__((ext_vector_type(4)));
+template <class T> constexpr bool is_float_acc = T(0.5) != T(0);
+
+// 16-bit storage: fp16 if f16, else bf16 (both conversions are computed and one
+// selected, so a uniform flag costs no branch).  fp32 -> 16 bit rounds to
+// nearest even.
+__device__ static inline float decode16(uint16_t h, bool f16) {
+    const float a = (float)__builtin_bit_cast(_Float16, h);
+    const float b = __builtin_bit_cast(float, (uint32_t)h << 16);
+    return f16 ? a : b;
+}
+__device__ static inline uint16_t encode16(float x, bool f16) {
+    const uint16_t a = __builtin_bit_cast(uint16_t, (_Float16)x);
+    const uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)x);
+    return f16 ? a : b;
+}
+
+// Four consecutive elements [idx, idx + 4) of one row, SZ bytes each in memory
+// (4: the accumulator type itself; 2: fp16 / bf16, float accumulators only).
+// n of them (0..4) lie inside the matrix; vec: one aligned vector access is allowed.
+template <class T, int SZ>
+__device__ static inline vec4_of<T> load4s(const void *base, int64_t idx, bool f16, bool vec, int n) {
+    vec4_of<T> r = {0, 0, 0, 0};
+    if constexpr (SZ == 4) {
+        const T *q = (const T *)base + idx;
+        if (vec && n == 4) return *(const vec4_of<T> *)q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) r[e] = q[e];
+    } else {
+        static_assert(is_float_acc<T>, "16-bit storage needs a float accumulator");
+        const uint16_t *q = (const uint16_t *)base + idx;
+        if (vec && n == 4) {
+            const ushortx4 h = *(const ushortx4 *)q;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = decode16(h[e], f16);
+            return r;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) r[e] = decode16(q[e], f16);
+    }
+    return r;
+}
+template <class T, int SZ>
+__device__ static inline void store4s(void *base, int64_t idx, vec4_of<T> v, bool f16, bool vec, int n) {
+    if constexpr (SZ == 4) {
+        T *q = (T *)base + idx;
+        if (vec && n == 4) {
+            *(vec4_of<T> *)q = v;
+            return;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) q[e] = v[e];
+    } else {
+        static_assert(is_float_acc<T>, "16-bit storage needs a float accumulator");
+        uint16_t *q = (uint16_t *)base + idx;
+        ushortx4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = encode16(v[e], f16);
+        if (vec && n == 4) {
+            *(ushortx4 *)q = h;
+            return;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < n) q[e] = h[e];
+    }
+}
+
+// The same with the storage type t (OUT_*) known only at run time.
+template <class T>
+__device__ static inline vec4_of<T> load4(const void *base, int64_t idx, int t, bool vec, int n) {
+    if constexpr (is_float_acc<T>) {
+        if (t != OUT_F32) return load4s<T, 2>(base, idx, t == OUT_F16, vec, n);
+    }
+    return load4s<T, 4>(base, idx, false, vec, n);
+}
+template <class T>
+__device__ static inline void store4(void *base, int64_t idx, vec4_of<T> v, int t, bool vec, int n) {
+    if constexpr (is_float_acc<T>) {
+        if (t != OUT_F32) return store4s<T, 2>(base, idx, v, t == OUT_F16, vec, n);
+    }
+    store4s<T, 4>(base, idx, v, false, vec, n);
+}
+
+// alpha * acc + beta * c, each product and the sum rounded separately.
+__device__ static inline floatx4 finish4(floatx4 acc, floatx4 c, const EpiParams &ep) {
+#pragma clang fp contract(off)
+    floatx4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float t = ep.alpha * acc[e];
+        r[e] = ep.use_c ? t + ep.beta * c[e] : t;
+    }
+    return r;
+}
+__device__ static inline intx4 finish4(intx4 acc, intx4 c, const EpiParams &ep) {
+    intx4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = ep.use_c ? add_acc(acc[e], c[e]) : acc[e];
+    return r;
 }
 
 __device__ static inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

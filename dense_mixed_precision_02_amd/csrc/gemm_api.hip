@@ -39,16 +39,39 @@ struct Plan {
 };
 
 int elem_size(int dtype) { return dtype == GEMM_I8 ? 1 : 2; }
+int out_bytes(int t) { return (t == GEMM_OUT_F16 || t == GEMM_OUT_BF16) ? 2 : 4; }
+
+// The plain output stage of gemm_run: D = acc + C in the accumulator type.
+EpiParams plain_epi(int dtype) {
+    EpiParams e;
+    e.alpha = 1.0f;
+    e.beta = 1.0f;
+    e.c_type = e.d_type = dtype == GEMM_I8 ? GEMM_OUT_I32 : GEMM_OUT_F32;
+    e.use_c = 1;
+    return e;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const void *D,
              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
-             unsigned flags, int64_t batch, bool check_ptrs) {
+             unsigned flags, int64_t batch, bool check_ptrs, const EpiParams &ep) {
     if (!h) return GEMM_ERR_INVALID_ARG;
     if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) return GEMM_ERR_INVALID_ARG;
     if (flags & ~(unsigned)(GEMM_A_COLMAJOR | GEMM_B_COLMAJOR)) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
+    // output stage: float inputs take fp32/fp16/bf16 C and D and any alpha, beta;
+    // int8 inputs take int32 C and D with alpha = 1 and beta in {0, 1}
+    if (dtype == GEMM_I8) {
+        if (ep.c_type != GEMM_OUT_I32 || ep.d_type != GEMM_OUT_I32 || ep.alpha != 1.0f ||
+            (ep.beta != 0.0f && ep.beta != 1.0f))
+            return GEMM_ERR_INVALID_ARG;
+    } else {
+        const auto float_type = [](int t) {
+            return t == GEMM_OUT_F32 || t == GEMM_OUT_F16 || t == GEMM_OUT_BF16;
+        };
+        if (!float_type(ep.c_type) || !float_type(ep.d_type)) return GEMM_ERR_INVALID_ARG;
+    }
     const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
     // A and B are not read when K == 0, so their leading dimensions are free then
     if (K > 0 && lda < std::max<int64_t>(1, a_col ? M : K)) return GEMM_ERR_INVALID_ARG;
@@ -60,10 +83,13 @@ int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const
         return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     if (!check_ptrs) return GEMM_OK;
-    if (!C || !D) return GEMM_ERR_INVALID_ARG;
+    if (!D || (ep.use_c && !C)) return GEMM_ERR_INVALID_ARG;
     if (K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
+    if (C == D && ep.use_c && ep.c_type != ep.d_type) return GEMM_ERR_INVALID_ARG;
     const uintptr_t es = (uintptr_t)elem_size(dtype);
-    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4) || ((uintptr_t)D % 4))
+    if (((uintptr_t)A % es) || ((uintptr_t)B % es) ||
+        (ep.use_c && ((uintptr_t)C % (uintptr_t)out_bytes(ep.c_type))) ||
+        ((uintptr_t)D % (uintptr_t)out_bytes(ep.d_type)))
         return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
@@ -197,24 +223,25 @@ int64_t reduce_grid(int64_t items) {
 
 template <class T>
 hipError_t launch_reduce_t(const void *W, const void *C, void *D, int64_t M, int64_t N, int64_t ldc,
-                           int64_t batch, int S, hipStream_t s) {
-    const bool vec = N % 4 == 0 && ldc % 4 == 0 && aligned16(C) && aligned16(D) &&
-                     (S == 0 || aligned16(W));
+                           int64_t batch, int S, const EpiParams &ep, hipStream_t s) {
+    const bool vec = N % 4 == 0 && ldc % 4 == 0 &&
+                     (!ep.use_c || (uintptr_t)C % (4u * out_bytes(ep.c_type)) == 0) &&
+                     (uintptr_t)D % (4u * out_bytes(ep.d_type)) == 0 && (S == 0 || aligned16(W));
     const int64_t elems = M * N * batch;
     if (vec)
         hipLaunchKernelGGL((splitk_reduce<T, true>), dim3((unsigned)reduce_grid(elems / 4)), dim3(256), 0,
-                           s, (const T *)W, (const T *)C, (T *)D, M, N, ldc, batch, S);
+                           s, (const T *)W, C, D, M, N, ldc, batch, S, ep);
     else
         hipLaunchKernelGGL((splitk_reduce<T, false>), dim3((unsigned)reduce_grid(elems)), dim3(256), 0, s,
-                           (const T *)W, (const T *)C, (T *)D, M, N, ldc, batch, S);
+                           (const T *)W, C, D, M, N, ldc, batch, S, ep);
     return hipGetLastError();
 }
 
-// Fixed-order sum of S split-K partials plus C into D (S == 0: D = C).
+// Fixed-order sum of S split-K partials, then the output stage, into D (S == 0: no partials).
 hipError_t launch_reduce(int dtype, const void *W, const void *C, void *D, int64_t M, int64_t N,
-                         int64_t ldc, int64_t batch, int S, hipStream_t s) {
-    if (dtype == GEMM_I8) return launch_reduce_t<int32_t>(W, C, D, M, N, ldc, batch, S, s);
-    return launch_reduce_t<float>(W, C, D, M, N, ldc, batch, S, s);
+                         int64_t ldc, int64_t batch, int S, const EpiParams &ep, hipStream_t s) {
+    if (dtype == GEMM_I8) return launch_reduce_t<int32_t>(W, C, D, M, N, ldc, batch, S, ep, s);
+    return launch_reduce_t<float>(W, C, D, M, N, ldc, batch, S, ep, s);
 }
 
 }  // namespace
@@ -269,7 +296,7 @@ int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int
     host_only.num_cus = 256;
     if (!h) h = &host_only;
     int rc = validate(h, nullptr, nullptr, nullptr, nullptr, M, N, K, lda, ldb, ldc, dtype, flags,
-                      batch, false);
+                      batch, false, plain_epi(dtype));
     if (rc != GEMM_OK) return rc;
     if (!label || label_len == 0) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) {
@@ -287,10 +314,17 @@ int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int
     return GEMM_OK;
 }
 
-int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
-             int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
-             unsigned flags, int64_t batch, void *stream) {
-    int rc = validate(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, true);
+int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
+                int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+                unsigned flags, int64_t batch, float alpha, float beta, int c_type, int d_type,
+                void *stream) {
+    EpiParams ep;
+    ep.alpha = alpha;
+    ep.beta = beta;
+    ep.c_type = c_type;
+    ep.d_type = d_type;
+    ep.use_c = beta != 0.0f;
+    int rc = validate(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, true, ep);
     if (rc != GEMM_OK) return rc;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     hipStream_t s = (hipStream_t)stream;
@@ -300,8 +334,9 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
     if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
 
     if (P.copy_only)
-        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, s) == hipSuccess ? GEMM_OK
-                                                                                     : GEMM_ERR_HIP;
+        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, ep, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
 
     if (P.cfg == CFG_GENERIC) {
         GenericArgs g;
@@ -313,6 +348,7 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
         g.b_cs = b_col ? ldb : 1;
         g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
         g.tiles_m = P.tiles_m; g.tiles_n = P.tiles_n;
+        g.ep = ep;
         const dim3 grid((unsigned)P.grid), blk(64);
         if (dtype == GEMM_F16) hipLaunchKernelGGL(generic_gemm<F16>, grid, blk, 0, s, g);
         else if (dtype == GEMM_BF16) hipLaunchKernelGGL(generic_gemm<BF16>, grid, blk, 0, s, g);
@@ -346,14 +382,23 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
     t.tiles_m = P.tiles_m; t.tiles_n = P.tiles_n;
     t.batch = (int)batch; t.splits = P.splits;
     t.partial = P.reduce ? 1 : 0;
+    t.ep = ep;
     hipError_t e;
     if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_col, P.grid, s);
     else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_col, P.grid, s);
     else e = launch_cfg<I8>(P.cfg, t, a_col, b_col, P.grid, s);
     if (e != hipSuccess) return GEMM_ERR_HIP;
-    if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, s) != hipSuccess)
+    if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, ep, s) != hipSuccess)
         return GEMM_ERR_HIP;
     return GEMM_OK;
+}
+
+int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
+             int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+             unsigned flags, int64_t batch, void *stream) {
+    const int t = dtype == GEMM_I8 ? GEMM_OUT_I32 : GEMM_OUT_F32;
+    return gemm_run_ex(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, 1.0f, 1.0f, t, t,
+                       stream);
 }
 
 }  // extern "C"

@@ -40,8 +40,15 @@ struct TileArgs {
     int64_t sA, sB, sC;      // batch strides in elements
     int64_t k_chunk;         // K elements per split (multiple of the k-tile)
     int tiles_m, tiles_n, batch, splits;
-    int partial;             // 1: write raw partials to W (split-K), 0: D = acc + C
+    int partial;             // 1: write raw partials to W (split-K), 0: output stage to D
+    EpiParams ep;            // output stage: alpha, beta, C and D storage types
 };
+
+// How many of the 4 columns starting at gcol lie inside N columns (0..4).
+__device__ static inline int cols_in(int64_t N, int64_t gcol) {
+    const int64_t r = N - gcol;
+    return r >= 4 ? 4 : (r <= 0 ? 0 : (int)r);
+}
 
 // Row swizzle of the K-contiguous LDS layout.  Any 8 consecutive rows (and the
 // even/odd rows of any 16) map to distinct 16-byte slots modulo 128 (256) bytes.
@@ -344,69 +351,96 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     constexpr int RPP = 64 / LPR;      // slab rows per pass
     constexpr int PASSES = 32 / RPP;
     const int64_t col_w = n0 + wn * WTN;
-    acc_t *Wb = p.partial ? (acc_t *)p.W + ((int64_t)split * p.batch + b) * p.M * p.N : nullptr;
-    const acc_t *Cb = (const acc_t *)p.C + (int64_t)b * p.sC;
-    acc_t *Db = (acc_t *)p.D + (int64_t)b * p.sC;
-    // 16-byte C/D accesses need 4-element alignment of every row start
+    // Split-K partials go to W (dense M x N per split and batch entry) unscaled:
+    // the output stage with alpha = 1 and no C leaves them unchanged.
+    EpiParams ep = p.ep;
+    if (p.partial) {
+        ep.alpha = 1.0f;
+        ep.use_c = 0;
+        ep.d_type = OUT_F32;
+    }
     const int64_t ldo = p.partial ? p.N : p.ldc;
-    const bool vec_ok = (ldo % 4 == 0) &&
-                        (p.partial ? ((uintptr_t)Wb % 16 == 0)
-                                   : ((uintptr_t)Cb % 16 == 0 && (uintptr_t)Db % 16 == 0));
+    const char *Cb = (const char *)p.C + (int64_t)b * p.sC * out_size(ep.c_type);
+    char *Ob = p.partial ? (char *)p.W + (((int64_t)split * p.batch + b) * p.M * p.N) * sizeof(acc_t)
+                         : (char *)p.D + (int64_t)b * p.sC * out_size(ep.d_type);
+    const bool c_f16 = ep.c_type == OUT_F16, d_f16 = ep.d_type == OUT_F16;
+    using vec4 = vec4_of<acc_t>;
+    // CS, DS: bytes per element of C (0: C not read) and of the output, fixed at
+    // compile time so that each variant is a short, fully unrolled loop.
+    auto epilogue = [&](auto cs_c, auto ds_c) {
+        constexpr int CS = decltype(cs_c)::value, DS = decltype(ds_c)::value;
+        // 4-element vector accesses need every row start aligned to 4 elements
+        const bool vec_ok = (ldo % 4 == 0) && (CS == 0 || (uintptr_t)Cb % (4 * CS) == 0) &&
+                            (uintptr_t)Ob % (4 * DS) == 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        // accumulators of rows [i*32, i*32+32) of the wave tile -> LDS, row-major
+        for (int i = 0; i < TM; ++i) {
+            // accumulators of rows [i*32, i*32+32) of the wave tile -> LDS, row-major
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-            for (int G = 0; G < 16; ++G)
-                slab[(8 * (G >> 2) + 4 * (lane >> 5) + (G & 3)) * SP + j * 32 + (lane & 31)] =
-                    acc[i][j][G];
-        // LDS instructions of one wave complete in order; this only keeps the
-        // compiler from moving the reads above the writes
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        const int64_t row_s = m0 + wm * WTM + i * 32;
-        typedef acc_t vec4 __attribute__((ext_vector_type(4)));
-        vec4 cv[PASSES];
-        // issue every C load of the slab before using any
-        if (!p.partial) {
+                for (int G = 0; G < 16; ++G)
+                    slab[(8 * (G >> 2) + 4 * (lane >> 5) + (G & 3)) * SP + j * 32 + (lane & 31)] =
+                        acc[i][j][G];
+            // LDS instructions of one wave complete in order; this only keeps the
+            // compiler from moving the reads above the writes
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const int64_t row_s = m0 + wm * WTM + i * 32;
+            if (vec_ok && row_s + 32 <= p.M && col_w + WTN <= p.N) {
+                // whole slab inside the matrix: straight-line vector code, with
+                // every C load of the slab issued before the first is used
+                vec4 cv[PASSES];
 #pragma unroll
-            for (int q = 0; q < PASSES; ++q) {
-                const int r = q * RPP + lane / LPR;
-                const int64_t grow = row_s + r, gcol = col_w + (lane % LPR) * 4;
-                const int64_t idx = grow * ldo + gcol;
-                if (vec_ok && grow < p.M && gcol + 3 < p.N) {
-                    cv[q] = *(const vec4 *)(Cb + idx);
-                } else {
+                for (int q = 0; q < PASSES; ++q) {
+                    cv[q] = vec4{0, 0, 0, 0};
+                    if constexpr (CS != 0) {
+                        const int64_t grow = row_s + q * RPP + lane / LPR;
+                        const int64_t gcol = col_w + (lane % LPR) * 4;
+                        cv[q] = load4s<acc_t, CS>(Cb, grow * ldo + gcol, c_f16, true, 4);
+                    }
+                }
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        cv[q][e] = (grow < p.M && gcol + e < p.N) ? Cb[idx + e] : acc_t(0);
+                for (int q = 0; q < PASSES; ++q) {
+                    const int r = q * RPP + lane / LPR;
+                    const int cl = (lane % LPR) * 4;
+                    const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+                    const int64_t grow = row_s + r, gcol = col_w + cl;
+                    store4s<acc_t, DS>(Ob, grow * ldo + gcol, finish4(v, cv[q], ep), d_f16, true, 4);
+                }
+            } else {
+                // edge slab (or unaligned rows): masked accesses, one pass at a time
+#pragma unroll 1
+                for (int q = 0; q < PASSES; ++q) {
+                    const int r = q * RPP + lane / LPR;
+                    const int cl = (lane % LPR) * 4;
+                    const int64_t grow = row_s + r, gcol = col_w + cl;
+                    const int n = grow < p.M ? cols_in(p.N, gcol) : 0;
+                    vec4 c = {0, 0, 0, 0};
+                    if constexpr (CS != 0) c = load4s<acc_t, CS>(Cb, grow * ldo + gcol, c_f16, vec_ok, n);
+                    const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+                    store4s<acc_t, DS>(Ob, grow * ldo + gcol, finish4(v, c, ep), d_f16, vec_ok, n);
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
-#pragma unroll
-        for (int q = 0; q < PASSES; ++q) {
-            const int r = q * RPP + lane / LPR;
-            const int cl = (lane % LPR) * 4;
-            const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
-            const int64_t grow = row_s + r, gcol = col_w + cl;
-            const int64_t idx = grow * ldo + gcol;
-            vec4 o;
-            if (p.partial) {
-                o = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = add_acc(v[e], cv[q][e]);
-            }
-            acc_t *dst = p.partial ? Wb : Db;
-            if (vec_ok && grow < p.M && gcol + 3 < p.N) {
-                *(vec4 *)(dst + idx) = o;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (grow < p.M && gcol + e < p.N) dst[idx + e] = o[e];
-            }
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S2 = std::integral_constant<int, 2>;
+    using S4 = std::integral_constant<int, 4>;
+    if constexpr (is_float_acc<acc_t>) {
+        const bool c16 = out_size(ep.c_type) == 2, d16 = out_size(ep.d_type) == 2;
+        if (!ep.use_c) {
+            if (d16) epilogue(S0{}, S2{});
+            else epilogue(S0{}, S4{});
+        } else if (c16) {
+            if (d16) epilogue(S2{}, S2{});
+            else epilogue(S2{}, S4{});
+        } else {
+            if (d16) epilogue(S4{}, S2{});
+            else epilogue(S4{}, S4{});
         }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    } else {
+        if (ep.use_c) epilogue(S4{}, S4{});
+        else epilogue(S0{}, S4{});
     }
 }
 

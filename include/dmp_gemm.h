@@ -90,6 +90,34 @@ int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void 
              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype, unsigned flags, int64_t batch, void *stream);
 
+/* Storage types of C and D for gemm_run_ex. */
+typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2, GEMM_OUT_I32 = 3 } gemm_out_t;
+
+/*
+ * Scaled product with a low-precision output (the fp16/bf16-result variants of
+ * the matrix instructions; pages: "RDNA3 dense WMMA builtins", FP16- and
+ * BF16-accumulate builtins, which keep the result in 16-bit storage).  For
+ * b < batch:
+ *
+ *     D_b = cvt_D( alpha * (A_b * B_b)  +  beta * cvt(C_b) )
+ *
+ * computed as: the fp32 accumulation of gemm_run, then t = alpha*acc and
+ * u = beta*c (each an fp32 round-to-nearest-even product; c decoded exactly
+ * from C's storage type), s = t + u (fp32 RNE add; no fused multiply-add), and
+ * finally s converted to D's storage type with round-to-nearest-even.
+ * beta == 0: C is not read (may be NULL) and D = cvt_D(alpha*acc).
+ * c_type, d_type: gemm_out_t.  fp16/bf16 inputs accept GEMM_OUT_F32, _F16 and
+ * _BF16 for each of C and D independently; int8 inputs require GEMM_OUT_I32
+ * for both, alpha == 1 and beta in {0, 1}.  C and D share ldc (in elements of
+ * their own type); D may alias C only when their types are equal.  All other
+ * arguments, layouts and errors are those of gemm_run, which equals
+ * gemm_run_ex with alpha = beta = 1 and C, D in the accumulator type.
+ */
+int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, void *D,
+                int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                int dtype, unsigned flags, int64_t batch, float alpha, float beta,
+                int c_type, int d_type, void *stream);
+
 /* Release the handle's workspace (after synchronising its device) and the handle. */
 int gemm_destroy(gemm_handle_t h);
 

@@ -169,6 +169,69 @@ def gemm_points(dtype: str, A, B, C, pts: np.ndarray, M: int, N: int, K: int,
     return Di if dtype == "i8" else (D, S)
 
 
+OUT_TYPES = {"f32": 0, "f16": 1, "bf16": 2, "i32": 3}
+# unit roundoff of the output storage type, and half its smallest subnormal spacing
+_OUT_UNIT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+_OUT_FLOOR = {"f32": 0.0, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}
+
+
+def decode_c(c_type: str, C: np.ndarray) -> np.ndarray:
+    """Exact float64 values of a C array stored as fp32 (float32), fp16 or bf16 (uint16 bits)."""
+    if c_type == "f32":
+        return np.asarray(C, dtype=np.float32).astype(np.float64)
+    table = decode(c_type, np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    return table[np.asarray(C, dtype=np.uint16)]
+
+
+# (significand bits incl. the leading one, smallest normal exponent, largest finite value)
+_FORMATS = {"f16": (11, -14, 65504.0), "bf16": (8, -126, float.fromhex("0x1.fep127")),
+            "f32": (24, -126, float.fromhex("0x1.fffffep127"))}
+
+
+def round_to(d_type: str, x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest value of fp16 / bf16 / fp32, ties to the even
+    significand (the IEEE default), returned as float64.  From the definition: the
+    spacing of representable values around x is 2^(max(e, emin) - p + 1), with e the
+    exponent of x; x is divided by that spacing, rounded half-to-even to an integer and
+    scaled back.  Magnitudes at or beyond max + spacing/2 become infinities."""
+    p, emin, vmax = _FORMATS[d_type]
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    xf = x[fin]
+    _, e2 = np.frexp(xf)                  # |x| = m * 2^e2 with m in [0.5, 1)
+    e = np.maximum(e2 - 1, emin)          # exponent of the leading bit, clamped to emin
+    spacing = np.ldexp(1.0, (e - p + 1).astype(np.int64))
+    r = np.round(xf / spacing) * spacing  # np.round: ties to even
+    top = vmax + np.ldexp(1.0, int(np.floor(np.log2(vmax))) - p)  # max + half its spacing
+    r = np.where(np.abs(xf) >= top, np.copysign(np.inf, xf), r)
+    out[fin] = r
+    return out
+
+
+def scaled_reference(P: np.ndarray, c_exact: np.ndarray, alpha: float, beta: float) -> np.ndarray:
+    """D_exact = alpha * (A B) + beta * C, with P = A B from gemm() run on a zero C (fp64)."""
+    out = float(alpha) * np.asarray(P, dtype=np.float64)
+    if beta != 0.0:
+        out = out + float(beta) * np.asarray(c_exact, dtype=np.float64)
+    return out
+
+
+def scaled_tolerance(K: int, S: np.ndarray, c_exact: np.ndarray, D_ref: np.ndarray,
+                     alpha: float, beta: float, d_type: str) -> np.ndarray:
+    """Bound on |D - D_exact| for the scaled, converted output stage:
+    fp32 accumulation (4*K*2^-24*S), the two fp32 products and the fp32 sum
+    (2^-24 of |alpha*S|, |beta*c| and of the sum each), and the final
+    round-to-nearest-even conversion (unit roundoff of D's type, plus half the
+    smallest fp16 subnormal spacing)."""
+    u = 2.0 ** -24
+    aS = abs(float(alpha)) * np.asarray(S, dtype=np.float64)
+    bc = abs(float(beta)) * np.abs(np.asarray(c_exact, dtype=np.float64)) if beta != 0 else 0.0
+    e_acc = abs(float(alpha)) * 4.0 * K * u * np.asarray(S, dtype=np.float64)
+    e_fp32 = e_acc + u * (aS + bc) + u * (np.abs(D_ref) + e_acc + 2 * u * (aS + bc))
+    return e_fp32 + _OUT_UNIT[d_type] * (np.abs(D_ref) + e_fp32) + _OUT_FLOOR[d_type]
+
+
 def float_tolerance(K: int, S: np.ndarray, C: np.ndarray) -> np.ndarray:
     """Per-element bound |D - D_ref| <= 4*K*2^-24*S + 2^-24*|c| for fp16/bf16 inputs
     accumulated in fp32, with C added once (the bound the fp paths are held to)."""

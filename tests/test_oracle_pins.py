@@ -314,3 +314,118 @@ def test_tolerance_accepts_fp32_and_rejects_dropped_term(dtype):
     assert np.all(np.abs(good - D[0]) <= tol)
     bad = fp32_sequential(p, drop_k=17).astype(np.float64)
     assert np.any(np.abs(bad - D[0]) > tol)
+
+
+# ------------------------------------------------------ scaled, converted output
+
+def _simulate_stage(acc32, c32, alpha, beta, d_type):
+    """The documented output stage in numpy: fp32 products and sum (no fused
+    multiply-add), then round-to-nearest-even to D's storage type."""
+    a = np.float32(alpha)
+    t = (a * acc32).astype(np.float32)
+    if beta != 0:
+        t = (t + (np.float32(beta) * c32).astype(np.float32)).astype(np.float32)
+    if d_type == "f32":
+        return t.astype(np.float64)
+    if d_type == "f16":
+        return t.astype(np.float16).astype(np.float64)
+    bits = synth.f32_to_bf16_bits(t)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("d_type", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("c_type", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("alpha,beta", [(1.0, 1.0), (0.75, -2.5), (-3.0, 0.0)])
+def test_scaled_output_tolerance(c_type, d_type, alpha, beta):
+    """The stage's fp32 + conversion roundings stay inside scaled_tolerance; a
+    stage that forgets beta, or truncates instead of rounding, leaves it."""
+    p = synth.make_problem("bf16", 20, 24, 40, seed=31)
+    P, S = oracle.gemm("bf16", p.A, p.B, np.zeros_like(p.C), **p.oracle_args())
+    P, S = P[0], S[0]
+    rng = np.random.default_rng(3)
+    cvals = rng.uniform(-4, 4, size=(20, 24))
+    if c_type == "f32":
+        Cst = cvals.astype(np.float32)
+    elif c_type == "f16":
+        Cst = synth.f64_to_f16_bits(cvals)
+    else:
+        Cst = synth.f32_to_bf16_bits(cvals.astype(np.float32))
+    c_exact = oracle.decode_c(c_type, Cst)
+    D_ref = oracle.scaled_reference(P, c_exact, alpha, beta)
+    tol = oracle.scaled_tolerance(p.K, S, c_exact, D_ref, alpha, beta, d_type)
+    acc32 = fp32_sequential(p)  # C of the generated problem is added at the end: remove it
+    acc32 = (acc32 - p.C[0]).astype(np.float32)
+    good = _simulate_stage(acc32, c_exact.astype(np.float32), alpha, beta, d_type)
+    assert np.all(np.abs(good - D_ref) <= tol)
+    if beta != 0:
+        no_beta = _simulate_stage(acc32, c_exact.astype(np.float32), alpha, 0.0, d_type)
+        assert np.any(np.abs(no_beta - D_ref) > tol)
+    if d_type == "bf16":
+        t = _simulate_stage(acc32, c_exact.astype(np.float32), alpha, beta, "f32").astype(np.float32)
+        trunc = ((t.view(np.uint32) >> 16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.any(np.abs(trunc - D_ref) > tol)
+
+
+def test_decode_c_matches_library():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    f = np.isfinite(bits.view(np.float16))
+    assert np.array_equal(oracle.decode_c("f16", bits)[f], bits.view(np.float16)[f].astype(np.float64))
+    x = np.float32([1.5, -2.25, 3e-20])
+    assert np.array_equal(oracle.decode_c("f32", x), x.astype(np.float64))
+
+
+# --------------------------------------------------- rounding to the output type
+
+def _all_values(d_type):
+    """Every finite value of a 16-bit format (decoded by the pinned decoder), sorted,
+    with its bit pattern."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = oracle.decode(d_type, bits)
+    ok = np.isfinite(v)
+    order = np.argsort(v[ok], kind="stable")
+    return v[ok][order], bits[ok][order]
+
+
+@pytest.mark.parametrize("d_type", ["f16", "bf16"])
+def test_round_to_brute_force_nearest(d_type):
+    """round_to picks the nearest representable value, and on an exact tie the one whose
+    bit pattern is even; found here by search over all 2^16 patterns."""
+    vals, bits = _all_values(d_type)
+    rng = np.random.default_rng(5)
+    finite_max = vals[-1]
+    mid = rng.integers(0, len(vals) - 1, 2000)
+    # random magnitudes over the whole range, exact midpoints, subnormals, near-overflow
+    x = np.concatenate([
+        rng.standard_normal(3000) * np.exp2(rng.integers(-30 if d_type == "f16" else -140,
+                                                         16 if d_type == "f16" else 127, 3000)),
+        (vals[mid] + vals[mid + 1]) / 2,
+        rng.uniform(-1, 1, 500) * vals[vals > 0][0] * 8,
+        np.array([finite_max * (1 + 2.0 ** -12), -finite_max * (1 - 2.0 ** -30), 0.0, -0.0]),
+    ])
+    x = x[np.abs(x) < finite_max]      # overflow is checked separately
+    got = oracle.round_to(d_type, x)
+    idx = np.searchsorted(vals, x)
+    lo = vals[np.clip(idx - 1, 0, len(vals) - 1)]
+    hi = vals[np.clip(idx, 0, len(vals) - 1)]
+    bhi = bits[np.clip(idx, 0, len(vals) - 1)]
+    dlo, dhi = np.abs(x - lo), np.abs(hi - x)
+    want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(bhi % 2 == 0, hi, lo)))
+    assert np.array_equal(got, want)   # == also equates the two zeros
+
+
+def test_round_to_matches_numpy_casts():
+    """float64 -> float16 and float64 -> float32 casts in numpy round to nearest even."""
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(20000) * np.exp2(rng.integers(-20, 15, 20000))
+    assert np.array_equal(oracle.round_to("f16", x), x.astype(np.float16).astype(np.float64))
+    y = rng.standard_normal(20000) * np.exp2(rng.integers(-140, 120, 20000))
+    assert np.array_equal(oracle.round_to("f32", y), y.astype(np.float32).astype(np.float64))
+
+
+@pytest.mark.parametrize("d_type,big", [("f16", 65520.0), ("bf16", float.fromhex("0x1.ffp127"))])
+def test_round_to_overflow_and_specials(d_type, big):
+    """max + half a spacing and beyond round to infinity; just below stays finite."""
+    vmax = 65504.0 if d_type == "f16" else float.fromhex("0x1.fep127")
+    r = oracle.round_to(d_type, np.array([big, -big, np.nextafter(big, 0), np.inf, np.nan]))
+    assert r[0] == np.inf and r[1] == -np.inf and r[2] == vmax
+    assert r[3] == np.inf and np.isnan(r[4])
