@@ -39,7 +39,10 @@ _lib = None
 def build() -> str:
     """Compile the oracle with the host C compiler (always rebuilds)."""
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-pthread", "-o", tmp, _SRC, "-lm"]
+    # no contraction of a*b+c into fma: the fp64 path's error-free transformations
+    # rely on every + and * rounding exactly once
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", "-pthread",
+           "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -72,6 +75,13 @@ def _load():
     lib.oracle_gemm_points.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp,
                                        i64, i64, i64, i64, i64, i64,
                                        ctypes.c_int, ctypes.c_int, i64, i64, i64, i64]
+    f64p = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+            i64, i64, i64, i64, ctypes.c_int]
+    lib.oracle_gemm_f64.restype = ctypes.c_int
+    lib.oracle_gemm_f64.argtypes = f64p
+    lib.oracle_gemm_f64_points.restype = ctypes.c_int
+    lib.oracle_gemm_f64_points.argtypes = [vp, vp, vp, vp, i64, vp, vp, vp, i64, i64, i64, i64,
+                                           i64, i64, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64]
     _lib = lib
     return lib
 
@@ -169,7 +179,67 @@ def gemm_points(dtype: str, A, B, C, pts: np.ndarray, M: int, N: int, K: int,
     return Di if dtype == "i8" else (D, S)
 
 
-OUT_TYPES = {"f32": 0, "f16": 1, "bf16": 2, "i32": 3}
+def _f64_args(A, B, C):
+    for x in (A, B, C):
+        assert x.dtype == np.float64 and x.flags["C_CONTIGUOUS"], "fp64 operands are float64"
+
+
+def gemm_f64(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, a_col: bool = False,
+             b_col: bool = False, batch: int = 1, sa: int | None = None, sb: int | None = None,
+             sc: int | None = None, nthreads: int | None = None):
+    """fp64 reference: returns (D_hi, D_lo, S), each float64 (batch, M, N); D_ref = D_hi + D_lo
+    to about 106 significant bits (double-double accumulation)."""
+    _f64_args(A, B, C)
+    lib = _load()
+    sa = (K * lda if a_col else M * lda) if sa is None else sa
+    sb = (N * ldb if b_col else K * ldb) if sb is None else sb
+    sc = M * ldc if sc is None else sc
+    nthreads = default_threads() if nthreads is None else nthreads
+    Dh = np.zeros((batch, M, N))
+    Dl = np.zeros((batch, M, N))
+    S = np.zeros((batch, M, N))
+    rc = lib.oracle_gemm_f64(_ptr(A), _ptr(B), _ptr(C), _ptr(Dh), _ptr(Dl), _ptr(S), M, N, K,
+                             lda, ldb, ldc, int(a_col), int(b_col), batch, sa, sb, sc, nthreads)
+    if rc:
+        raise ValueError("oracle_gemm_f64 rejected its arguments")
+    return Dh, Dl, S
+
+
+def gemm_f64_points(A, B, C, pts, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                    a_col: bool = False, b_col: bool = False, batch: int = 1,
+                    sa: int | None = None, sb: int | None = None, sc: int | None = None):
+    """fp64 reference at the listed (b, i, j) positions: (D_hi, D_lo, S) vectors."""
+    _f64_args(A, B, C)
+    lib = _load()
+    pts = np.ascontiguousarray(pts, dtype=np.int64).reshape(-1, 3)
+    n = pts.shape[0]
+    sa = (K * lda if a_col else M * lda) if sa is None else sa
+    sb = (N * ldb if b_col else K * ldb) if sb is None else sb
+    sc = M * ldc if sc is None else sc
+    Dh, Dl, S = np.zeros(n), np.zeros(n), np.zeros(n)
+    rc = lib.oracle_gemm_f64_points(_ptr(A), _ptr(B), _ptr(C), _ptr(pts), n, _ptr(Dh), _ptr(Dl),
+                                    _ptr(S), M, N, K, lda, ldb, ldc, int(a_col), int(b_col), batch,
+                                    sa, sb, sc)
+    if rc:
+        raise ValueError("oracle_gemm_f64_points rejected its arguments")
+    return Dh, Dl, S
+
+
+def f64_error(D: np.ndarray, D_hi: np.ndarray, D_lo: np.ndarray) -> np.ndarray:
+    """|D - (D_hi + D_lo)| evaluated without losing D_lo (D - D_hi is exact when close)."""
+    return np.abs((np.asarray(D, dtype=np.float64) - D_hi) - D_lo)
+
+
+def f64_tolerance(K: int, S: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """Bound for fp64 inputs with an fp64 accumulator that rounds to nearest even
+    (each product and each addition at most half an ulp): (2K+2)*2^-53*S for the
+    reduction, with a factor 2 for any summation order, and 2^-53*|c| for the one
+    final addition of C."""
+    u = 2.0 ** -53
+    return (2.0 * K + 2.0) * u * np.asarray(S, dtype=np.float64) + u * np.abs(np.asarray(C, dtype=np.float64))
+
+
+OUT_TYPES = {"f32": 0, "f16": 1, "bf16": 2, "i32": 3, "f64": 4}
 # unit roundoff of the output storage type, and half its smallest subnormal spacing
 _OUT_UNIT = {"f32": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 _OUT_FLOOR = {"f32": 0.0, "f16": 2.0 ** -25, "bf16": 2.0 ** -134}

@@ -27,6 +27,14 @@
  * The i-k-j loop order keeps B accesses contiguous for row-major B; there is
  * no blocking or reordering beyond that.  Rows are split over threads.
  *
+ * fp64 inputs (pages: "CDNA2 dense MFMA builtins", section "FP64-accumulate
+ * builtins": one double per lane for A and B, a double accumulator) are not
+ * exactly multipliable in double, so that path keeps every product and every
+ * partial sum as an unevaluated pair hi + lo (double-double): the product's
+ * rounding error is recovered exactly with a fused multiply-add and each
+ * addition's with Knuth's two-sum, so the result carries about 106 significant
+ * bits -- exact for practical purposes next to the fp64 tolerance.
+ *
  * Layout of the inputs (same convention as the GPU library):
  *   A row-major: A[i][k] at A[i*lda + k]   col-major: A[i + k*lda]
  *   B row-major: B[k][j] at B[k*ldb + j]   col-major: B[k + j*ldb]
@@ -236,6 +244,145 @@ int oracle_gemm_int8(const int8_t *A, const int8_t *B, const int32_t *C, int64_t
     pthread_mutex_init(&J.lock, NULL);
     run_threads(&J, int_worker, nthreads);
     pthread_mutex_destroy(&J.lock);
+    return 0;
+}
+
+/* ---- fp64 inputs -------------------------------------------------------- */
+
+/* a + b = *s + *e exactly (Knuth's two-sum; valid for any ordering of |a|, |b|). */
+static void two_sum(double a, double b, double *s, double *e)
+{
+    const double x = a + b;
+    const double bv = x - a;
+    const double av = x - bv;
+    *s = x;
+    *e = (a - av) + (b - bv);
+}
+
+/* a * b = *p + *e exactly (fma rounds once, so it returns the exact residual). */
+static void two_prod(double a, double b, double *p, double *e)
+{
+    const double x = a * b;
+    *p = x;
+    *e = fma(a, b, -x);
+}
+
+/* (hi, lo) += v + w, keeping the rounding error of the leading addition. */
+static void dd_add(double *hi, double *lo, double v, double w)
+{
+    double s, e;
+    two_sum(*hi, v, &s, &e);
+    *hi = s;
+    *lo += e + w;
+}
+
+typedef struct {
+    const double *A, *B, *C;
+    double *Dhi, *Dlo, *S;
+    int64_t M, N, K, lda, ldb, ldc;
+    int a_col, b_col;
+    int64_t batch, sa, sb, sc;
+    int64_t next_row;
+    pthread_mutex_t lock;
+} job64_t;
+
+static void *f64_worker(void *arg)
+{
+    job64_t *J = (job64_t *)arg;
+    const int64_t N = J->N, K = J->K;
+    double *hi = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    double *lo = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    double *sab = (double *)calloc((size_t)(N > 0 ? N : 1), sizeof(double));
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        const int64_t r = J->next_row++;
+        pthread_mutex_unlock(&J->lock);
+        if (r >= J->batch * J->M) break;
+        const int64_t b = r / J->M, i = r % J->M;
+        const double *Ab = J->A + b * J->sa;
+        const double *Bb = J->B + b * J->sb;
+        for (int64_t j = 0; j < N; ++j) { hi[j] = 0.0; lo[j] = 0.0; sab[j] = 0.0; }
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = J->a_col ? Ab[i + k * J->lda] : Ab[i * J->lda + k];
+            for (int64_t j = 0; j < N; ++j) {
+                const double bv = J->b_col ? Bb[k + j * J->ldb] : Bb[k * J->ldb + j];
+                double p, pe;
+                two_prod(a, bv, &p, &pe);
+                dd_add(&hi[j], &lo[j], p, pe);
+                sab[j] += fabs(p);
+            }
+        }
+        const double *Cb = J->C + b * J->sc;
+        for (int64_t j = 0; j < N; ++j) {
+            dd_add(&hi[j], &lo[j], Cb[i * J->ldc + j], 0.0);
+            two_sum(hi[j], lo[j], &J->Dhi[r * N + j], &J->Dlo[r * N + j]);
+            J->S[r * N + j] = sab[j];
+        }
+    }
+    free(hi);
+    free(lo);
+    free(sab);
+    return NULL;
+}
+
+/*
+ * fp64 path: D_ref = C + sum_k A B as the pair Dhi + Dlo (|Dlo| <= ulp(Dhi)/2),
+ * and S = sum_k |a*b| (plain double).  Same layouts and outputs as the float path.
+ */
+int oracle_gemm_f64(const double *A, const double *B, const double *C, double *Dhi,
+                    double *Dlo, double *S, int64_t M, int64_t N, int64_t K, int64_t lda,
+                    int64_t ldb, int64_t ldc, int a_col, int b_col, int64_t batch, int64_t sa,
+                    int64_t sb, int64_t sc, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;
+    job64_t J;
+    memset(&J, 0, sizeof(J));
+    J.A = A; J.B = B; J.C = C; J.Dhi = Dhi; J.Dlo = Dlo; J.S = S;
+    J.M = M; J.N = N; J.K = K; J.lda = lda; J.ldb = ldb; J.ldc = ldc;
+    J.a_col = a_col; J.b_col = b_col; J.batch = batch; J.sa = sa; J.sb = sb; J.sc = sc;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, f64_worker, &J) != 0) break;
+        ++started;
+    }
+    if (started == 0) f64_worker(&J);
+    for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+    pthread_mutex_destroy(&J.lock);
+    return 0;
+}
+
+/* fp64 path at listed (b, i, j) positions only. */
+int oracle_gemm_f64_points(const double *A, const double *B, const double *C,
+                           const int64_t *pts, int64_t npts, double *Dhi, double *Dlo, double *S,
+                           int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                           int64_t ldc, int a_col, int b_col, int64_t batch, int64_t sa,
+                           int64_t sb, int64_t sc)
+{
+    if (K < 0) return -1;
+    for (int64_t p = 0; p < npts; ++p) {
+        const int64_t b = pts[3 * p], i = pts[3 * p + 1], j = pts[3 * p + 2];
+        if (b < 0 || b >= batch || i < 0 || i >= M || j < 0 || j >= N) return -1;
+    }
+    for (int64_t p = 0; p < npts; ++p) {
+        const int64_t b = pts[3 * p], i = pts[3 * p + 1], j = pts[3 * p + 2];
+        const double *Ab = A + b * sa, *Bb = B + b * sb;
+        double hi = 0.0, lo = 0.0, sab = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = a_col ? Ab[i + k * lda] : Ab[i * lda + k];
+            const double bv = b_col ? Bb[k + j * ldb] : Bb[k * ldb + j];
+            double q, qe;
+            two_prod(a, bv, &q, &qe);
+            dd_add(&hi, &lo, q, qe);
+            sab += fabs(q);
+        }
+        dd_add(&hi, &lo, C[b * sc + i * ldc + j], 0.0);
+        two_sum(hi, lo, &Dhi[p], &Dlo[p]);
+        S[p] = sab;
+    }
     return 0;
 }
 

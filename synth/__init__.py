@@ -8,7 +8,7 @@ the binary32 pattern), and lays them out in memory.
 
 Storage conventions (the same on both sides):
   * fp16 / bf16 inputs are uint16 bit patterns; fp32 C is float32;
-    int8 inputs are int8, int32 C is int32;
+    int8 inputs are int8, int32 C is int32; fp64 A, B and C are float64;
   * A row-major -> memory shape (batch, M, lda); col-major -> (batch, K, lda);
   * B row-major -> (batch, K, ldb);  col-major -> (batch, N, ldb);
   * C and D row-major -> (batch, M, ldc);  consecutive batches are contiguous.
@@ -19,7 +19,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-ACC_DTYPE = {"f16": np.float32, "bf16": np.float32, "i8": np.int32}
+ACC_DTYPE = {"f16": np.float32, "bf16": np.float32, "i8": np.int32, "f64": np.float64}
 
 
 @dataclass
@@ -76,6 +76,8 @@ def _draw(rng: np.random.Generator, dtype: str, dist: str, shape, lo=None, hi=No
         v = rng.integers(-1, 1, size=shape, endpoint=True).astype(np.float64)
     else:
         raise ValueError(dist)
+    if dtype == "f64":
+        return np.asarray(v, dtype=np.float64)
     if dtype == "f16":
         return f64_to_f16_bits(v)
     return f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
@@ -88,12 +90,13 @@ def _draw_c(rng, dtype: str, dist: str, shape, lo=None, hi=None):
         if dist == "uniform_int":
             return rng.integers(lo, hi, size=shape, endpoint=True, dtype=np.int32)
         raise ValueError(dist)
+    ct = np.float64 if dtype == "f64" else np.float32
     if dist == "zeros":
-        return np.zeros(shape, dtype=np.float32)
+        return np.zeros(shape, dtype=ct)
     if dist == "uniform":
-        return rng.uniform(lo, hi, size=shape).astype(np.float32)
+        return rng.uniform(lo, hi, size=shape).astype(ct)
     if dist == "small_int":
-        return rng.integers(lo, hi, size=shape, endpoint=True).astype(np.float32)
+        return rng.integers(lo, hi, size=shape, endpoint=True).astype(ct)
     raise ValueError(dist)
 
 
@@ -143,6 +146,10 @@ CONFIGS = {
     # supplementary: 4096^3 fp16 with C1's distributions
     "S1": dict(dtype="f16", M=4096, N=4096, K=4096, seed=6, ab_dist="uniform",
                ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
+    # fp64 (the double-precision instruction family): 4096^3, A/B row-major
+    # uniform[-1,1], C fp64 uniform[-1,1]
+    "F1": dict(dtype="f64", M=4096, N=4096, K=4096, seed=7, ab_dist="uniform",
+               ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
 }
 
 CONFIG_LABELS = {
@@ -152,6 +159,7 @@ CONFIG_LABELS = {
     "C4": "batched gemm 8192 x 64x64x64 fp16 (row-major), C fp32",
     "C5": "gemm 1024x1024x65536 bf16 (row-major), C fp32 zeros",
     "S1": "gemm 4096x4096x4096 fp16 (row-major), C fp32",
+    "F1": "gemm 4096x4096x4096 fp64 (row-major), C fp64",
 }
 
 

@@ -429,3 +429,104 @@ def test_round_to_overflow_and_specials(d_type, big):
     r = oracle.round_to(d_type, np.array([big, -big, np.nextafter(big, 0), np.inf, np.nan]))
     assert r[0] == np.inf and r[1] == -np.inf and r[2] == vmax
     assert r[3] == np.inf and np.isnan(r[4])
+
+
+# ------------------------------------------------------------------ fp64 path
+
+def f64_logical(p, b):
+    A, B = p.A[b], p.B[b]
+    A = A[:p.K, :p.M].T if p.a_col else A[:p.M, :p.K]
+    B = B[:p.N, :p.K].T if p.b_col else B[:p.K, :p.N]
+    return A, B, p.C[b][:p.M, :p.N]
+
+
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_f64_brute_force_exact(a_col, b_col):
+    """Rational brute force: D_hi + D_lo equals the exact value to ~2^-100 relative."""
+    rng = np.random.default_rng(21)
+    for trial in range(5):
+        M, N, K = (int(x) for x in rng.integers(1, 8, size=3))
+        p = synth.make_problem("f64", M, N, K, batch=2, a_col=a_col, b_col=b_col,
+                               pad=int(rng.integers(0, 3)), seed=300 + trial)
+        # spread the exponents so that products are not exact in fp64
+        p.A *= np.exp2(rng.integers(-30, 30, size=p.A.shape))
+        Dh, Dl, S = oracle.gemm_f64(p.A, p.B, p.C, **p.oracle_args())
+        for b in range(2):
+            A, B, C = f64_logical(p, b)
+            for i in range(M):
+                for j in range(N):
+                    ex = Fraction(float(C[i, j])) + sum(Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+                                                        for k in range(K))
+                    s_ex = sum(abs(Fraction(float(A[i, k])) * Fraction(float(B[k, j]))) for k in range(K))
+                    got = Fraction(float(Dh[b, i, j])) + Fraction(float(Dl[b, i, j]))
+                    assert abs(got - ex) <= Fraction(2) ** -100 * (s_ex + abs(Fraction(float(C[i, j])))) 
+                    assert abs(Fraction(float(S[b, i, j])) - s_ex) <= K * Fraction(2) ** -52 * s_ex
+
+
+def test_f64_cancellation_needs_the_low_part():
+    """1e16 + 1 - 1e16 (+ 0.5 from C): plain fp64 summation loses the 1, the pair keeps it."""
+    A = np.array([[[1e16, 1.0, -1e16]]])
+    B = np.array([[[1.0], [1.0], [1.0]]])
+    C = np.array([[[0.5]]])
+    Dh, Dl, S = oracle.gemm_f64(A, B, C, M=1, N=1, K=3, lda=3, ldb=1, ldc=1)
+    assert Dh[0, 0, 0] + Dl[0, 0, 0] == 1.5 and Dh[0, 0, 0] == 1.5
+    assert S[0, 0, 0] == 2e16 + 1
+    # the rounding error of a single product is recovered too: (1 + 2^-30)^2
+    x = 1.0 + 2.0 ** -30
+    Dh, Dl, _ = oracle.gemm_f64(np.array([[[x]]]), np.array([[[x]]]), np.zeros((1, 1, 1)),
+                                M=1, N=1, K=1, lda=1, ldb=1, ldc=1)
+    assert Fraction(float(Dh[0, 0, 0])) + Fraction(float(Dl[0, 0, 0])) == Fraction(x) ** 2
+
+
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_f64_against_numpy_and_closed_forms(a_col, b_col):
+    p = synth.make_problem("f64", 37, 53, 71, batch=2, a_col=a_col, b_col=b_col, pad=3, seed=22)
+    Dh, Dl, S = oracle.gemm_f64(p.A, p.B, p.C, **p.oracle_args(), nthreads=3)
+    for b in range(2):
+        A, B, C = f64_logical(p, b)
+        ref = A @ B + C
+        assert np.all(np.abs(Dh[b] - ref) <= 2 * p.K * 2.0 ** -52 * (np.abs(A) @ np.abs(B) + np.abs(C)))
+    # identity and permutation: exact
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((9, 9))
+    P = np.eye(9)[rng.permutation(9)]
+    for L, R in [(X, np.eye(9)), (np.eye(9), X), (P, X), (X, P)]:
+        Dh, Dl, _ = oracle.gemm_f64(L[None].copy(), R[None].copy(), np.zeros((1, 9, 9)),
+                                    M=9, N=9, K=9, lda=9, ldb=9, ldc=9)
+        assert np.array_equal(Dh[0], L @ R) and np.all(Dl == 0)
+    # rank one with powers of two: K * x_i * y_j + c exactly
+    x = np.exp2(rng.integers(-20, 20, 6)).astype(np.float64)
+    y = np.exp2(rng.integers(-20, 20, 5)).astype(np.float64)
+    K = 11
+    A = np.repeat(x[:, None], K, axis=1)[None].copy()
+    B = np.repeat(y[None, :], K, axis=0)[None].copy()
+    C = rng.integers(-9, 9, (1, 6, 5)).astype(np.float64)
+    Dh, Dl, _ = oracle.gemm_f64(A, B, C, M=6, N=5, K=K, lda=K, ldb=5, ldc=5)
+    want = [[Fraction(K) * Fraction(x[i]) * Fraction(y[j]) + Fraction(C[0, i, j]) for j in range(5)]
+            for i in range(6)]
+    for i in range(6):
+        for j in range(5):
+            assert Fraction(float(Dh[0, i, j])) + Fraction(float(Dl[0, i, j])) == want[i][j]
+
+
+def test_f64_points_match_full():
+    p = synth.make_problem("f64", 23, 19, 45, batch=3, b_col=True, pad=1, seed=23)
+    Dh, Dl, S = oracle.gemm_f64(p.A, p.B, p.C, **p.oracle_args())
+    pts = np.array([(b, i, j) for b in range(3) for i in (0, 7, 22) for j in (0, 5, 18)])
+    ph, pl, ps = oracle.gemm_f64_points(p.A, p.B, p.C, pts, **p.oracle_args())
+    sel = (pts[:, 0], pts[:, 1], pts[:, 2])
+    assert np.array_equal(ph, Dh[sel]) and np.array_equal(pl, Dl[sel]) and np.array_equal(ps, S[sel])
+
+
+def test_f64_tolerance_accepts_fp64_sum_and_rejects_dropped_term():
+    p = synth.make_problem("f64", 16, 16, 512, seed=24)
+    Dh, Dl, S = oracle.gemm_f64(p.A, p.B, p.C, **p.oracle_args())
+    A, B, C = f64_logical(p, 0)
+    seq = np.zeros((16, 16))
+    for k in range(p.K):             # plain sequential fp64, C added last
+        seq = seq + np.outer(A[:, k], B[k, :])
+    seq = seq + C
+    tol = oracle.f64_tolerance(p.K, S[0], C)
+    assert np.all(oracle.f64_error(seq, Dh[0], Dl[0]) <= tol)
+    dropped = seq - np.outer(A[:, 100], B[100, :])
+    assert np.any(oracle.f64_error(dropped, Dh[0], Dl[0]) > tol)

@@ -61,3 +61,15 @@ def test_exact_variant_is_small_integers(name):
     vals = p.A.view(np.float16).astype(np.float64)
     assert set(np.unique(vals)).issubset({-1.0, 0.0, 1.0})
     assert np.all(p.C == np.round(p.C)) and np.abs(p.C).max() <= 8
+
+
+def test_f64_problem_storage():
+    p = synth.make_problem("f64", 5, 7, 9, b_col=True, pad=2, seed=9)
+    assert p.A.dtype == np.float64 and p.B.dtype == np.float64 and p.C.dtype == np.float64
+    assert p.A.shape == (1, 5, 11) and p.B.shape == (1, 7, 11) and p.C.shape == (1, 5, 9)
+    assert p.A.min() >= -1 and p.A.max() < 1 and len(np.unique(p.A)) == p.A.size
+    f = synth.make_problem("f64", 4, 4, 4, seed=9, ab_dist="small_int", c_dist="small_int",
+                           c_range=(-8, 8))
+    assert set(np.unique(f.A)) <= {-1.0, 0.0, 1.0} and np.all(f.C == np.round(f.C))
+    q = synth.CONFIGS["F1"]
+    assert (q["dtype"], q["M"], q["N"], q["K"]) == ("f64", 4096, 4096, 4096)
