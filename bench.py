@@ -26,10 +26,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # Published MI355X dense peaks (256 CUs x 2.4 GHz): fp16/bf16 4096 FLOP/clk/CU,
-# int8 8192 OP/clk/CU; HBM3E 8 TB/s.
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2}
+# int8 8192 OP/clk/CU, fp64 matrix 128 FLOP/clk/CU; HBM3E 8 TB/s.
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f64": 78.6}
 PEAK_HBM_GBS = 8000.0
-DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2}
+DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # Configs whose bounding roof is HBM rather than the matrix cores (arithmetic
 # intensity below the ~315 FLOP/byte ridge).
 HBM_BOUND = {"C4"}
@@ -69,6 +69,11 @@ def cpu_baseline(p, budget_s: float = 15.0):
     import oracle
     threads = min(oracle.default_threads(), 16)
 
+    def ref(dtype, A, B, C, **kw):
+        if dtype == "f64":
+            return oracle.gemm_f64(A, B, C, **kw)
+        return oracle.gemm(dtype, A, B, C, **kw)
+
     def run_rows(r):
         if p.batch > 1:
             nb = max(1, min(p.batch, r))
@@ -76,8 +81,8 @@ def cpu_baseline(p, budget_s: float = 15.0):
             B = p.B[:nb]
             C = p.C[:nb]
             t = time.perf_counter()
-            oracle.gemm(p.dtype, A, B, C, M=p.M, N=p.N, K=p.K, lda=p.lda, ldb=p.ldb, ldc=p.ldc,
-                        a_col=p.a_col, b_col=p.b_col, batch=nb, nthreads=threads)
+            ref(p.dtype, A, B, C, M=p.M, N=p.N, K=p.K, lda=p.lda, ldb=p.ldb, ldc=p.ldc,
+                a_col=p.a_col, b_col=p.b_col, batch=nb, nthreads=threads)
             return time.perf_counter() - t, 2 * nb * p.M * p.N * p.K, f"{nb} of {p.batch} batch entries"
         r = max(1, min(p.M, r))
         if p.a_col:
@@ -89,9 +94,8 @@ def cpu_baseline(p, budget_s: float = 15.0):
             C = np.ascontiguousarray(p.C[:, :r, :])
             M = r
         t = time.perf_counter()
-        oracle.gemm(p.dtype, A, p.B, C, M=M, N=p.N, K=p.K, lda=p.lda, ldb=p.ldb, ldc=p.ldc,
-                    a_col=p.a_col, b_col=p.b_col, batch=1, sa=0 if p.a_col else None,
-                    nthreads=threads)
+        ref(p.dtype, A, p.B, C, M=M, N=p.N, K=p.K, lda=p.lda, ldb=p.ldb, ldc=p.ldc,
+            a_col=p.a_col, b_col=p.b_col, batch=1, sa=0 if p.a_col else None, nthreads=threads)
         return time.perf_counter() - t, 2 * M * p.N * p.K, f"rows 0..{M - 1} of {p.M}"
 
     # calibrate on a small sample, then size the measured sample to ~budget_s
@@ -125,6 +129,11 @@ def parity_sample(p, D_host, ex=None):
         Dref = oracle.scaled_reference(P, c, alpha, beta)
         tol = oracle.scaled_tolerance(p.K, S, c, Dref, alpha, beta, d_type)
         ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+        return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
+    if p.dtype == "f64":
+        Dh, Dl, S = oracle.gemm_f64_points(p.A, p.B, p.C, pts, **p.oracle_args())
+        tol = oracle.f64_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
+        ratio = float(np.max(oracle.f64_error(Dg, Dh, Dl) / tol))
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     r = oracle.gemm_points(p.dtype, p.A, p.B, p.C, pts, **p.oracle_args())
     if p.dtype == "i8":

@@ -8,9 +8,9 @@ import threading
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libdmp_gemm.so"
 
-GEMM_F16, GEMM_BF16, GEMM_I8 = 0, 1, 2
+GEMM_F16, GEMM_BF16, GEMM_I8, GEMM_F64 = 0, 1, 2, 3
 GEMM_A_COLMAJOR, GEMM_B_COLMAJOR = 1, 2
-GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32 = 0, 1, 2, 3
+GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32, GEMM_OUT_F64 = 0, 1, 2, 3, 4
 GEMM_OK = 0
 
 EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy",
@@ -154,24 +154,27 @@ def _operand_layout(X, rows: int, cols: int, name: str):
 def _out_code(dtype):
     import torch
     return {torch.float32: GEMM_OUT_F32, torch.float16: GEMM_OUT_F16,
-            torch.bfloat16: GEMM_OUT_BF16, torch.int32: GEMM_OUT_I32}.get(dtype)
+            torch.bfloat16: GEMM_OUT_BF16, torch.int32: GEMM_OUT_I32,
+            torch.float64: GEMM_OUT_F64}.get(dtype)
 
 
 def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtype=None,
          handle: Handle | None = None):
     """D = alpha * (A @ B) + beta * C on the current stream.
 
-    A: (..., M, K) float16 / bfloat16 / int8;  B: (..., K, N) same dtype (row-major, or a
-    transposed view = column-major);  C: (..., M, N) row-major, float32 / float16 / bfloat16
-    for float inputs, int32 for int8 (None means beta = 0).  D has ``out_dtype`` (default:
-    float32, int32 for int8), a new tensor with C's strides unless ``out`` is given (``out``
-    may be C itself when the dtypes agree).  Leading batch dims (one at most) must be
-    contiguous in the library's sense.  int8 takes alpha == 1 and beta in {0, 1} only."""
+    A: (..., M, K) float16 / bfloat16 / int8 / float64;  B: (..., K, N) same dtype (row-major,
+    or a transposed view = column-major);  C: (..., M, N) row-major, float32 / float16 /
+    bfloat16 for 16-bit inputs, int32 for int8, float64 for float64 (None means beta = 0).
+    D has ``out_dtype`` (default: float32; int32 for int8; float64 for float64), a new tensor
+    with C's strides unless ``out`` is given (``out`` may be C itself when the dtypes agree).
+    Leading batch dims (one at most) must be contiguous in the library's sense.  int8 and
+    float64 take alpha == 1 and beta in {0, 1} only."""
     import torch
-    dt = {torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16, torch.int8: GEMM_I8}.get(A.dtype)
+    dt = {torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16, torch.int8: GEMM_I8,
+          torch.float64: GEMM_F64}.get(A.dtype)
     if dt is None or B.dtype != A.dtype:
-        raise TypeError("A and B must both be float16, bfloat16 or int8")
-    acc = torch.int32 if dt == GEMM_I8 else torch.float32
+        raise TypeError("A and B must both be float16, bfloat16, int8 or float64")
+    acc = {GEMM_I8: torch.int32, GEMM_F64: torch.float64}.get(dt, torch.float32)
     if A.dim() != B.dim() or A.dim() not in (2, 3):
         raise ValueError("A and B must both be 2-D or both 3-D")
     if not (A.is_cuda and B.is_cuda):
@@ -188,7 +191,7 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
             raise ValueError("C must be a GPU tensor of shape (..., M, N)")
         if C.stride(-1) != 1:
             raise ValueError("C must be row-major")
-    c_code = _out_code(C.dtype) if C is not None else (GEMM_OUT_I32 if dt == GEMM_I8 else GEMM_OUT_F32)
+    c_code = _out_code(C.dtype if C is not None else acc)
     if c_code is None:
         raise TypeError("C must be float32, float16, bfloat16 or int32")
     d_dtype = out.dtype if out is not None else (out_dtype if out_dtype is not None else acc)

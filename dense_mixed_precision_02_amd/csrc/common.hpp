@@ -100,6 +100,7 @@ __device__ static inline void wait_vmcnt() {
 // int32 add that wraps modulo 2^32 (done in unsigned arithmetic, where wrapping
 // is defined).
 __device__ static inline float add_acc(float a, float b) { return a + b; }
+__device__ static inline double add_acc(double a, double b) { return a + b; }
 __device__ static inline int32_t add_acc(int32_t a, int32_t b) {
     return (int32_t)((uint32_t)a + (uint32_t)b);
 }
@@ -111,7 +112,7 @@ __device__ static inline int32_t add_acc(int32_t a, int32_t b) {
 // rounding to nearest even.  alpha = beta = 1 with fp32 C and D is the plain
 // D = acc + C.  The int8 path only has D = acc + C (int32, wrapping) or D = acc.
 // ---------------------------------------------------------------------------
-enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3 };
+enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3, OUT_F64 = 4 };
 
 struct EpiParams {
     float alpha, beta;
@@ -119,7 +120,9 @@ struct EpiParams {
     int use_c;  // beta != 0: C is read
 };
 
-__device__ static inline int out_size(int t) { return (t == OUT_F16 || t == OUT_BF16) ? 2 : 4; }
+__device__ static inline int out_size(int t) {
+    return (t == OUT_F16 || t == OUT_BF16) ? 2 : t == OUT_F64 ? 8 : 4;
+}
 
 typedef uint16_t ushortx4 __attribute__((ext_vector_type(4)));
 template <class T> using vec4_of = T __attribute__((ext_vector_type(4)));
@@ -140,12 +143,12 @@ __device__ static inline uint16_t encode16(float x, bool f16) {
 }
 
 // Four consecutive elements [idx, idx + 4) of one row, SZ bytes each in memory
-// (4: the accumulator type itself; 2: fp16 / bf16, float accumulators only).
+// (sizeof(T): the accumulator type itself; 2: fp16 / bf16, float accumulators only).
 // n of them (0..4) lie inside the matrix; vec: one aligned vector access is allowed.
 template <class T, int SZ>
 __device__ static inline vec4_of<T> load4s(const void *base, int64_t idx, bool f16, bool vec, int n) {
     vec4_of<T> r = {0, 0, 0, 0};
-    if constexpr (SZ == 4) {
+    if constexpr (SZ == sizeof(T)) {
         const T *q = (const T *)base + idx;
         if (vec && n == 4) return *(const vec4_of<T> *)q;
 #pragma unroll
@@ -168,7 +171,7 @@ __device__ static inline vec4_of<T> load4s(const void *base, int64_t idx, bool f
 }
 template <class T, int SZ>
 __device__ static inline void store4s(void *base, int64_t idx, vec4_of<T> v, bool f16, bool vec, int n) {
-    if constexpr (SZ == 4) {
+    if constexpr (SZ == sizeof(T)) {
         T *q = (T *)base + idx;
         if (vec && n == 4) {
             *(vec4_of<T> *)q = v;
@@ -196,17 +199,17 @@ __device__ static inline void store4s(void *base, int64_t idx, vec4_of<T> v, boo
 // The same with the storage type t (OUT_*) known only at run time.
 template <class T>
 __device__ static inline vec4_of<T> load4(const void *base, int64_t idx, int t, bool vec, int n) {
-    if constexpr (is_float_acc<T>) {
+    if constexpr (sizeof(T) == 4 && is_float_acc<T>) {
         if (t != OUT_F32) return load4s<T, 2>(base, idx, t == OUT_F16, vec, n);
     }
-    return load4s<T, 4>(base, idx, false, vec, n);
+    return load4s<T, sizeof(T)>(base, idx, false, vec, n);
 }
 template <class T>
 __device__ static inline void store4(void *base, int64_t idx, vec4_of<T> v, int t, bool vec, int n) {
-    if constexpr (is_float_acc<T>) {
+    if constexpr (sizeof(T) == 4 && is_float_acc<T>) {
         if (t != OUT_F32) return store4s<T, 2>(base, idx, v, t == OUT_F16, vec, n);
     }
-    store4s<T, 4>(base, idx, v, false, vec, n);
+    store4s<T, sizeof(T)>(base, idx, v, false, vec, n);
 }
 
 // alpha * acc + beta * c, each product and the sum rounded separately.
@@ -217,6 +220,18 @@ __device__ static inline floatx4 finish4(floatx4 acc, floatx4 c, const EpiParams
     for (int e = 0; e < 4; ++e) {
         const float t = ep.alpha * acc[e];
         r[e] = ep.use_c ? t + ep.beta * c[e] : t;
+    }
+    return r;
+}
+// fp64: only alpha = 1 and beta in {0, 1} reach here, so this is acc (+ c).
+__device__ static inline vec4_of<double> finish4(vec4_of<double> acc, vec4_of<double> c,
+                                                 const EpiParams &ep) {
+#pragma clang fp contract(off)
+    vec4_of<double> r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const double t = (double)ep.alpha * acc[e];
+        r[e] = ep.use_c ? t + (double)ep.beta * c[e] : t;
     }
     return r;
 }

@@ -10,6 +10,7 @@
 
 #include "../../include/dmp_gemm.h"
 #include "aux_kernels.hpp"
+#include "dgemm.hpp"
 #include "tile_gemm.hpp"
 
 using namespace dmp;
@@ -23,8 +24,10 @@ struct gemm_handle {
 
 namespace {
 
-// Workgroup tile shapes of the tiled kernel (4 waves each, 2 x 2).
-enum Cfg { CFG_L = 0, CFG_M = 1, CFG_S = 2, CFG_GENERIC = 3 };
+// Workgroup tile shapes of the tiled kernel (4 waves each, 2 x 2); the fp64
+// kernels have their own.
+enum Cfg { CFG_L = 0, CFG_M = 1, CFG_S = 2, CFG_GENERIC = 3, CFG_D128 = 4, CFG_D64 = 5,
+           CFG_DGENERIC = 6 };
 constexpr int CFG_EDGE[3] = {256, 128, 64};
 
 struct Plan {
@@ -38,15 +41,20 @@ struct Plan {
     size_t ws_needed = 0;
 };
 
-int elem_size(int dtype) { return dtype == GEMM_I8 ? 1 : 2; }
-int out_bytes(int t) { return (t == GEMM_OUT_F16 || t == GEMM_OUT_BF16) ? 2 : 4; }
+int elem_size(int dtype) { return dtype == GEMM_I8 ? 1 : dtype == GEMM_F64 ? 8 : 2; }
+int out_bytes(int t) {
+    return (t == GEMM_OUT_F16 || t == GEMM_OUT_BF16) ? 2 : t == GEMM_OUT_F64 ? 8 : 4;
+}
+int acc_type(int dtype) {
+    return dtype == GEMM_I8 ? GEMM_OUT_I32 : dtype == GEMM_F64 ? GEMM_OUT_F64 : GEMM_OUT_F32;
+}
 
 // The plain output stage of gemm_run: D = acc + C in the accumulator type.
 EpiParams plain_epi(int dtype) {
     EpiParams e;
     e.alpha = 1.0f;
     e.beta = 1.0f;
-    e.c_type = e.d_type = dtype == GEMM_I8 ? GEMM_OUT_I32 : GEMM_OUT_F32;
+    e.c_type = e.d_type = acc_type(dtype);
     e.use_c = 1;
     return e;
 }
@@ -57,13 +65,16 @@ int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const
              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
              unsigned flags, int64_t batch, bool check_ptrs, const EpiParams &ep) {
     if (!h) return GEMM_ERR_INVALID_ARG;
-    if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) return GEMM_ERR_INVALID_ARG;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8 && dtype != GEMM_F64)
+        return GEMM_ERR_INVALID_ARG;
     if (flags & ~(unsigned)(GEMM_A_COLMAJOR | GEMM_B_COLMAJOR)) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
-    // output stage: float inputs take fp32/fp16/bf16 C and D and any alpha, beta;
-    // int8 inputs take int32 C and D with alpha = 1 and beta in {0, 1}
-    if (dtype == GEMM_I8) {
-        if (ep.c_type != GEMM_OUT_I32 || ep.d_type != GEMM_OUT_I32 || ep.alpha != 1.0f ||
+    // output stage: fp16/bf16 inputs take fp32/fp16/bf16 C and D and any alpha,
+    // beta; int8 and fp64 inputs keep C and D in their accumulator type, with
+    // alpha = 1 and beta in {0, 1}
+    if (dtype == GEMM_I8 || dtype == GEMM_F64) {
+        const int t = acc_type(dtype);
+        if (ep.c_type != t || ep.d_type != t || ep.alpha != 1.0f ||
             (ep.beta != 0.0f && ep.beta != 1.0f))
             return GEMM_ERR_INVALID_ARG;
     } else {
@@ -118,6 +129,31 @@ bool granule_ok(const void *A, const void *B, int64_t M, int64_t N, int64_t K, i
     return span_a < lim && span_b < lim;
 }
 
+// fp64: 128 x 128 tiles when they fill the device, else 64 x 64; the
+// element-wise kernel when the 16-byte granule path cannot take the operands.
+Plan make_plan_f64(const gemm_handle *h, const void *A, const void *B, int64_t M, int64_t N,
+                   int64_t K, int64_t lda, int64_t ldb, bool a_col, bool b_col, int64_t batch,
+                   bool check_ptrs) {
+    Plan P;
+    if (!granule_ok(A, B, M, N, K, lda, ldb, GEMM_F64, a_col, b_col, check_ptrs)) {
+        P.cfg = CFG_DGENERIC;
+        P.tiles_m = (int)cdiv(M, 16);
+        P.tiles_n = (int)cdiv(N, 16);
+        P.grid = (int64_t)P.tiles_m * P.tiles_n * batch;
+        return P;
+    }
+    const int64_t cus = h->num_cus > 0 ? h->num_cus : 256;
+    const int64_t t128 = cdiv(M, 128) * cdiv(N, 128) * batch;
+    const double useful128 = (double)M * (double)N / ((double)cdiv(M, 128) * 128.0 *
+                                                      (double)cdiv(N, 128) * 128.0);
+    const int e = (t128 >= cus && useful128 >= 0.75) ? 128 : 64;
+    P.cfg = e == 128 ? CFG_D128 : CFG_D64;
+    P.tiles_m = (int)cdiv(M, e);
+    P.tiles_n = (int)cdiv(N, e);
+    P.grid = (int64_t)P.tiles_m * P.tiles_n * batch;
+    return P;
+}
+
 Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, int64_t N, int64_t K,
                int64_t lda, int64_t ldb, int dtype, unsigned flags, int64_t batch, bool check_ptrs) {
     Plan P;
@@ -126,6 +162,7 @@ Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, in
         P.copy_only = true;
         return P;
     }
+    if (dtype == GEMM_F64) return make_plan_f64(h, A, B, M, N, K, lda, ldb, a_col, b_col, batch, check_ptrs);
     const int es = elem_size(dtype);
     const int64_t kt = 128 / es;
     if (!granule_ok(A, B, M, N, K, lda, ldb, dtype, a_col, b_col, check_ptrs)) {
@@ -184,11 +221,48 @@ const char *cfg_name(int cfg) {
     case CFG_L: return "tile256x256";
     case CFG_M: return "tile128x128";
     case CFG_S: return "tile64x64";
+    case CFG_D128: return "dtile128x128";
+    case CFG_D64: return "dtile64x64";
+    case CFG_DGENERIC: return "dgeneric16x16";
     default: return "generic32x32";
     }
 }
 
-const char *dtype_name(int d) { return d == GEMM_F16 ? "f16" : d == GEMM_BF16 ? "bf16" : "i8"; }
+const char *dtype_name(int d) {
+    return d == GEMM_F16 ? "f16" : d == GEMM_BF16 ? "bf16" : d == GEMM_F64 ? "f64" : "i8";
+}
+
+template <int E, bool AK, bool BKC>
+hipError_t launch_dgemm_t(const DgemmArgs &a, int64_t grid, hipStream_t s) {
+    hipLaunchKernelGGL((dgemm_tile<E, E, AK, BKC>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_dgemm_layout(const DgemmArgs &a, bool a_col, bool b_col, int64_t grid,
+                               hipStream_t s) {
+    if (!a_col && b_col) return launch_dgemm_t<E, true, true>(a, grid, s);
+    if (!a_col && !b_col) return launch_dgemm_t<E, true, false>(a, grid, s);
+    if (a_col && b_col) return launch_dgemm_t<E, false, true>(a, grid, s);
+    return launch_dgemm_t<E, false, false>(a, grid, s);
+}
+
+// fp64 launch for plan P (tile or element-wise kernel).
+hipError_t launch_f64(const Plan &P, const void *A, const void *B, const void *C, void *D,
+                      int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                      bool a_col, bool b_col, int64_t sA, int64_t sB, int64_t sC, int use_c,
+                      hipStream_t s) {
+    DgemmArgs a;
+    a.A = (const double *)A; a.B = (const double *)B; a.C = (const double *)C; a.D = (double *)D;
+    a.M = M; a.N = N; a.K = K; a.lda = lda; a.ldb = ldb; a.ldc = ldc;
+    a.sA = sA; a.sB = sB; a.sC = sC;
+    a.tiles_m = P.tiles_m; a.tiles_n = P.tiles_n;
+    a.use_c = use_c;
+    if (P.cfg == CFG_D128) return launch_dgemm_layout<128>(a, a_col, b_col, P.grid, s);
+    if (P.cfg == CFG_D64) return launch_dgemm_layout<64>(a, a_col, b_col, P.grid, s);
+    hipLaunchKernelGGL(dgemm_generic, dim3((unsigned)P.grid), dim3(64), 0, s, a, (int)a_col, (int)b_col);
+    return hipGetLastError();
+}
 
 template <class DT, int BM, int BN, bool AK, bool BKC>
 hipError_t launch_tile(const TileArgs &a, int64_t grid, hipStream_t s) {
@@ -241,6 +315,7 @@ hipError_t launch_reduce_t(const void *W, const void *C, void *D, int64_t M, int
 hipError_t launch_reduce(int dtype, const void *W, const void *C, void *D, int64_t M, int64_t N,
                          int64_t ldc, int64_t batch, int S, const EpiParams &ep, hipStream_t s) {
     if (dtype == GEMM_I8) return launch_reduce_t<int32_t>(W, C, D, M, N, ldc, batch, S, ep, s);
+    if (dtype == GEMM_F64) return launch_reduce_t<double>(W, C, D, M, N, ldc, batch, S, ep, s);
     return launch_reduce_t<float>(W, C, D, M, N, ldc, batch, S, ep, s);
 }
 
@@ -338,6 +413,12 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
                    ? GEMM_OK
                    : GEMM_ERR_HIP;
 
+    if (dtype == GEMM_F64)
+        return launch_f64(P, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
+                          ep.use_c, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+
     if (P.cfg == CFG_GENERIC) {
         GenericArgs g;
         g.A = A; g.B = B; g.C = C; g.D = D;
@@ -396,7 +477,7 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
 int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
              int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
              unsigned flags, int64_t batch, void *stream) {
-    const int t = dtype == GEMM_I8 ? GEMM_OUT_I32 : GEMM_OUT_F32;
+    const int t = acc_type(dtype);
     return gemm_run_ex(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, 1.0f, 1.0f, t, t,
                        stream);
 }

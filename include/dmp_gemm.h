@@ -17,11 +17,16 @@
  *   GEMM_F16   IEEE binary16         float (fp32)        fp32 (MFMA)
  *   GEMM_BF16  bfloat16              float (fp32)        fp32 (MFMA)
  *   GEMM_I8    int8 (signed)         int32               int32 (MFMA), exact
+ *   GEMM_F64   IEEE binary64         double (fp64)       fp64 (MFMA), every step
+ *                                                        rounded to nearest even
  *
  * int8 results are exact whenever the true result fits in int32 (the
  * accumulation wraps modulo 2^32, which is associative, so partial sums may
  * overflow as long as the final value fits).  fp16/bf16 results satisfy, per
- * element, |D - D_exact| <= 4*K*2^-24 * sum_k |a_ik b_kj| + 2^-24 * |c_ij|.
+ * element, |D - D_exact| <= 4*K*2^-24 * sum_k |a_ik b_kj| + 2^-24 * |c_ij|;
+ * fp64 results satisfy |D - D_exact| <= (2K+2)*2^-53 * sum_k |a_ik b_kj| +
+ * 2^-53 * |c_ij| (pages: "CDNA2 dense MFMA builtins", section "FP64-accumulate
+ * builtins": the FP64 instructions round partial products to nearest even).
  *
  * Memory layout (element strides, not bytes):
  *   A row-major (default):        A[i][k] at A[i*lda + k], lda >= K
@@ -56,7 +61,7 @@ extern "C" {
 
 typedef struct gemm_handle *gemm_handle_t;
 
-typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_I8 = 2 } gemm_dtype_t;
+typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_I8 = 2, GEMM_F64 = 3 } gemm_dtype_t;
 
 /* flags: bitwise OR; default (0) is row-major A and row-major B. */
 enum { GEMM_A_COLMAJOR = 1u, GEMM_B_COLMAJOR = 2u };
@@ -82,16 +87,20 @@ int gemm_create(gemm_handle_t *out);
  * M, N, K, batch >= 0.  M, N or batch == 0 is a no-op returning GEMM_OK.
  * K == 0 gives D = C (A, B and their leading dimensions are then not used).
  * dtype: a gemm_dtype_t.  flags: GEMM_A_COLMAJOR |
- * GEMM_B_COLMAJOR.  Any pointer alignment and leading dimension is accepted;
- * 16-byte aligned pointers with leading dimensions that are multiples of 16
- * bytes take the fast tiled path.
+ * GEMM_B_COLMAJOR.  Pointers must be aligned to their element size; any such
+ * pointer and any leading dimension is accepted, and 16-byte aligned pointers
+ * with leading dimensions that are multiples of 16 bytes take the fast tiled
+ * path (for K-contiguous operands K, for M/N-contiguous ones M or N, must also
+ * be a whole number of 16-byte granules).
  */
 int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D,
              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype, unsigned flags, int64_t batch, void *stream);
 
 /* Storage types of C and D for gemm_run_ex. */
-typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2, GEMM_OUT_I32 = 3 } gemm_out_t;
+typedef enum {
+    GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2, GEMM_OUT_I32 = 3, GEMM_OUT_F64 = 4
+} gemm_out_t;
 
 /*
  * Scaled product with a low-precision output (the fp16/bf16-result variants of
@@ -108,7 +117,8 @@ typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_F16 = 1, GEMM_OUT_BF16 = 2, GEMM_OUT_I
  * beta == 0: C is not read (may be NULL) and D = cvt_D(alpha*acc).
  * c_type, d_type: gemm_out_t.  fp16/bf16 inputs accept GEMM_OUT_F32, _F16 and
  * _BF16 for each of C and D independently; int8 inputs require GEMM_OUT_I32
- * for both, alpha == 1 and beta in {0, 1}.  C and D share ldc (in elements of
+ * for both, fp64 inputs GEMM_OUT_F64 for both, and each of them alpha == 1 and
+ * beta in {0, 1}.  C and D share ldc (in elements of
  * their own type); D may alias C only when their types are equal.  All other
  * arguments, layouts and errors are those of gemm_run, which equals
  * gemm_run_ex with alpha = beta = 1 and C, D in the accumulator type.

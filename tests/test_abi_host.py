@@ -62,7 +62,8 @@ def plan_status(*args):
     (4, 4, 8, 8, 7, 4, 0, 2, 1),           # ldb < K (col-major B)
     (5, 4, 8, 4, 4, 4, 0, 1, 1),           # lda < M (col-major A)
     (4, 6, 8, 8, 6, 5, 0, 0, 1),           # ldc < N
-    (4, 4, 8, 8, 4, 4, 3, 0, 1),           # bad dtype
+    (4, 4, 8, 8, 4, 4, 5, 0, 1),           # bad dtype
+    (4, 4, 8, 8, 4, 4, -1, 0, 1),          # bad dtype
     (4, 4, 8, 8, 4, 4, 0, 4, 1),           # unknown flag bit
     (4, 4, 8, 8, 4, 4, 0, 0, -1),          # negative batch
 ])
@@ -106,3 +107,20 @@ def test_generic_path_when_granules_do_not_fit():
     # an MN-contiguous extent that is not whole granules -> element-wise path
     assert dmp.plan_label(60, 64, 32, 64, 64, 64, dmp.GEMM_F16,
                           dmp.GEMM_A_COLMAJOR).startswith("generic32x32")
+
+
+def test_f64_plans():
+    # 4096^3 fp64: 128 x 128 tiles (1024 of them, two per CU resident)
+    assert dmp.plan_label(4096, 4096, 4096, 4096, 4096, 4096, dmp.GEMM_F64) == \
+        "dtile128x128 f64 a:row b:row splitk=1 grid=1024"
+    # fewer 128-tiles than CUs -> 64 x 64
+    assert dmp.plan_label(512, 512, 512, 512, 512, 512, dmp.GEMM_F64).startswith("dtile64x64")
+    # odd K with K-contiguous A, odd leading dimension, odd M with column-major A
+    assert dmp.plan_label(64, 64, 31, 31, 64, 64, dmp.GEMM_F64).startswith("dgeneric16x16")
+    assert dmp.plan_label(64, 64, 64, 65, 64, 64, dmp.GEMM_F64).startswith("dgeneric16x16")
+    assert dmp.plan_label(63, 64, 64, 64, 64, 64, dmp.GEMM_F64,
+                          dmp.GEMM_A_COLMAJOR).startswith("dgeneric16x16")
+    # MN-contiguous operands only: odd K is fine on the tiled path
+    assert dmp.plan_label(64, 64, 31, 64, 64, 64, dmp.GEMM_F64,
+                          dmp.GEMM_A_COLMAJOR).startswith("dtile64x64")
+    assert plan_status(4, 4, 0, 1, 4, 4, dmp.GEMM_F64, 0, 1) == (0, "copy_c k=0")

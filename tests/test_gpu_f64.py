@@ -1,0 +1,228 @@
+"""GPU parity of the fp64 path (GEMM_F64) against the double-double oracle.
+
+Per element |D - D_ref| <= (2K+2)*2^-53*S + 2^-53*|c| (the fp64 instruction
+rounds every step to nearest even); inputs whose every partial sum is an
+integer below 2^53 must match bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import log, sample_points
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+F64 = 3
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_mixed_precision_02_amd as dmp
+    h = dmp.Handle()
+    yield h
+    h.close()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def flags_of(p):
+    return (1 if p.a_col else 0) | (2 if p.b_col else 0)
+
+
+def run(handle, p, tensors=None, D=None):
+    A, B, C = tensors if tensors is not None else (dev(p.A), dev(p.B), dev(p.C))
+    if D is None:
+        D = torch.empty_like(C)
+    handle.run(A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(), p.M, p.N, p.K, p.lda,
+               p.ldb, p.ldc, F64, flags_of(p), p.batch, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return D
+
+
+def logical(p, X):
+    return np.asarray(X).reshape(p.batch, p.M, p.ldc)[:, :, :p.N]
+
+
+def check_full(p, D, exact=False):
+    Dg = logical(p, D.cpu().numpy())
+    Dh, Dl, S = oracle.gemm_f64(p.A, p.B, p.C, **p.oracle_args())
+    assert np.all(np.isfinite(Dg))
+    if exact:
+        bad = np.argwhere((Dg != Dh) | (Dl != 0))
+        assert bad.size == 0, f"{len(bad)} mismatches on exact inputs, first at {bad[0]}"
+        return 0.0
+    err = oracle.f64_error(Dg, Dh, Dl)
+    tol = oracle.f64_tolerance(p.K, S, logical(p, p.C))
+    bad = np.argwhere(err > tol)
+    assert bad.size == 0, f"{len(bad)} over the bound, first at {bad[0]}"
+    return float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+def check_points(p, D, pts, exact=False):
+    Dg = logical(p, D.cpu().numpy())[pts[:, 0], pts[:, 1], pts[:, 2]]
+    Dh, Dl, S = oracle.gemm_f64_points(p.A, p.B, p.C, pts, **p.oracle_args())
+    if exact:
+        assert np.array_equal(Dg, Dh) and np.all(Dl == 0), "mismatch at sampled points"
+        return 0.0
+    c = p.C.reshape(p.batch, p.M, p.ldc)[pts[:, 0], pts[:, 1], pts[:, 2]]
+    err = oracle.f64_error(Dg, Dh, Dl)
+    tol = oracle.f64_tolerance(p.K, S, c)
+    assert np.all(err <= tol), f"over the bound at sampled points: {np.max(err / tol):.3g}"
+    return float(np.max(err / tol))
+
+
+def check_row_sums(p, D, exact=False):
+    """sum_j D_ij = sum_j C_ij + sum_k A_ik (sum_j B_kj) for every row: any dropped or
+    doubled tile or k-tile breaks it."""
+    Dg = logical(p, D.cpu().numpy())
+    for b in range(p.batch):
+        A = p.A[b][:p.K, :p.M].T if p.a_col else p.A[b][:p.M, :p.K]
+        B = p.B[b][:p.N, :p.K].T if p.b_col else p.B[b][:p.K, :p.N]
+        C = p.C[b][:p.M, :p.N]
+        want = C.sum(1) + A @ B.sum(1)
+        got = Dg[b].sum(1)
+        if exact:
+            assert np.array_equal(got, want), f"row sums differ in batch {b}"
+            continue
+        sabs = np.abs(A) @ np.abs(B).sum(1)
+        u = 2.0 ** -53
+        tol = (2 * p.K + 2) * u * sabs + u * np.abs(C).sum(1) \
+            + 4 * (p.N + p.K) * u * (sabs + np.abs(C).sum(1) + np.abs(got))
+        assert np.all(np.abs(got - want) <= tol), f"row sums over the bound in batch {b}"
+
+
+def test_workload_4096_cubed(handle):
+    import dense_mixed_precision_02_amd as dmp
+    p = synth.config_problem("F1")
+    lbl = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, F64, flags_of(p))
+    log(f"[f64] {synth.CONFIG_LABELS['F1']} plan={lbl}")
+    assert lbl.startswith("dtile128x128")
+    D = run(handle, p)
+    r = check_points(p, D, sample_points(p, 3000, seed=71))
+    check_row_sums(p, D)
+    log(f"[f64] ok, max err/bound {r:.3g}")
+
+
+def test_workload_exact_integer_inputs(handle):
+    p = synth.exact_variant("F1")
+    D = run(handle, p)
+    check_points(p, D, sample_points(p, 1000, seed=72), exact=True)
+    check_row_sums(p, D, exact=True)
+
+
+SHAPES = [(1, 1, 1), (7, 9, 4), (16, 16, 16), (33, 65, 24), (130, 66, 136), (257, 264, 200),
+          (300, 520, 1040), (64, 64, 31), (63, 62, 33)]
+
+
+@pytest.mark.parametrize("a_col,b_col", [(False, False), (False, True), (True, False), (True, True)])
+def test_ragged_shapes_all_layouts(handle, a_col, b_col):
+    import dense_mixed_precision_02_amd as dmp
+    for n, (M, N, K) in enumerate(SHAPES):
+        for pad in (0, 1):
+            p = synth.make_problem("f64", M, N, K, a_col=a_col, b_col=b_col, pad=pad, seed=80 + n)
+            lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, F64, flags_of(p))
+            log(f"[f64-ragged] {M}x{N}x{K} pad={pad} a_col={a_col} b_col={b_col} {lbl}")
+            check_full(p, run(handle, p))
+            e = synth.make_problem("f64", M, N, K, a_col=a_col, b_col=b_col, pad=pad,
+                                   seed=90 + n, ab_dist="small_int", c_dist="small_int",
+                                   c_range=(-8, 8))
+            check_full(e, run(handle, e), exact=True)
+
+
+def test_paths_covered():
+    """The ragged set reaches the 64x64 tile and the element-wise kernel in every layout."""
+    import dense_mixed_precision_02_amd as dmp
+    seen = set()
+    for a_col in (False, True):
+        for b_col in (False, True):
+            for (M, N, K) in SHAPES:
+                for pad in (0, 1):
+                    lda = (M if a_col else K) + pad
+                    ldb = (K if b_col else N) + pad
+                    fl = (1 if a_col else 0) | (2 if b_col else 0)
+                    seen.add(dmp.plan_label(M, N, K, lda, ldb, N + pad, F64, fl).split()[0])
+    assert {"dtile64x64", "dgeneric16x16"} <= seen
+
+
+def test_batched_and_large_tiles(handle):
+    for (M, N, K, batch) in [(64, 64, 64, 300), (40, 72, 48, 5), (512, 512, 256, 4)]:
+        p = synth.make_problem("f64", M, N, K, batch=batch, b_col=True, seed=73)
+        log(f"[f64-batched] {batch} x {M}x{N}x{K}")
+        check_full(p, run(handle, p))
+
+
+def test_k_zero_beta_zero_alias_and_invalid(handle):
+    # K = 0: D = C exactly
+    p = synth.make_problem("f64", 33, 45, 0, batch=2, seed=74)
+    A, B, C = dev(p.A), dev(p.B), dev(p.C)
+    D = torch.full_like(C, 7.0)
+    run(handle, p, tensors=(A, B, C), D=D)
+    assert torch.equal(D, C)
+    # beta = 0 with a NULL C
+    q = synth.make_problem("f64", 200, 136, 96, seed=75)
+    A, B = dev(q.A), dev(q.B)
+    D = torch.empty((1, q.M, q.ldc), dtype=torch.float64, device="cuda")
+    handle.run_ex(A.data_ptr(), B.data_ptr(), 0, D.data_ptr(), q.M, q.N, q.K, q.lda, q.ldb, q.ldc,
+                  F64, 0, 1, alpha=1.0, beta=0.0, c_type=4, d_type=4,
+                  stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    Dh, Dl, S = oracle.gemm_f64(q.A, q.B, np.zeros_like(q.C), **q.oracle_args())
+    assert np.all(oracle.f64_error(D.cpu().numpy(), Dh, Dl) <= oracle.f64_tolerance(q.K, S, 0.0))
+    # D aliasing C
+    C = dev(q.C)
+    run(handle, q, tensors=(A, B, C), D=C)
+    check_full(q, C)
+    # invalid output-stage arguments for fp64 inputs enqueue nothing
+    Dd = torch.full((1, q.M, q.ldc), 3.0, dtype=torch.float64, device="cuda")
+    for kw in [dict(c_type=0, d_type=0), dict(c_type=4, d_type=0), dict(alpha=2.0),
+               dict(beta=0.5)]:
+        a = dict(alpha=1.0, beta=1.0, c_type=4, d_type=4)
+        a.update(kw)
+        rc = handle.status_ex(A.data_ptr(), B.data_ptr(), C.data_ptr(), Dd.data_ptr(), q.M, q.N,
+                              q.K, q.lda, q.ldb, q.ldc, F64, 0, 1, stream=0, **a)
+        assert rc == 1, kw
+    rc = handle.status(A.data_ptr() + 4, B.data_ptr(), C.data_ptr(), Dd.data_ptr(), q.M, q.N,
+                       q.K, q.lda, q.ldb, q.ldc, F64, 0, 1, 0)
+    assert rc == 1  # A not aligned to its element size
+    torch.cuda.synchronize()
+    assert torch.all(Dd == 3.0)
+
+
+def test_misaligned_operands_take_the_element_path(handle):
+    """8-byte but not 16-byte aligned A and B."""
+    p = synth.make_problem("f64", 96, 96, 128, seed=76)
+    A = torch.empty(p.A.size + 1, dtype=torch.float64, device="cuda")
+    B = torch.empty(p.B.size + 1, dtype=torch.float64, device="cuda")
+    A[1:] = dev(p.A).reshape(-1)
+    B[1:] = dev(p.B).reshape(-1)
+    C = dev(p.C)
+    D = torch.empty_like(C)
+    handle.run(A.data_ptr() + 8, B.data_ptr() + 8, C.data_ptr(), D.data_ptr(), p.M, p.N, p.K,
+               p.lda, p.ldb, p.ldc, F64, 0, 1, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    check_full(p, D)
+
+
+def test_run_to_run_bit_identical(handle):
+    p = synth.make_problem("f64", 1024, 1024, 2048, seed=77)
+    T = (dev(p.A), dev(p.B), dev(p.C))
+    D1 = run(handle, p, tensors=T).clone()
+    D2 = run(handle, p, tensors=T)
+    assert torch.equal(D1, D2)
+
+
+def test_torch_front_end(handle):
+    import dense_mixed_precision_02_amd as dmp
+    p = synth.make_problem("f64", 200, 136, 256, b_col=True, seed=78)
+    A = dev(p.A[0])
+    Bt = dev(p.B[0])       # (N, K): its transpose is a column-major (K, N) view
+    C = dev(p.C[0])
+    out = dmp.gemm(A, Bt.t(), C)
+    assert out.dtype == torch.float64
+    check_full(p, out[None])
