@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0
 DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # Configs whose bounding roof is HBM rather than the matrix cores (arithmetic
 # intensity below the ~315 FLOP/byte ridge).
-HBM_BOUND = {"C4"}
+HBM_BOUND = {"C4", "T1"}
 METRIC = "GEMM TFLOPS/TOPS (fp16, bf16, int8) on 1 MI355X; % of dense MFMA peak"
 COPY_BYTES = 512 << 20
 # rocprofv3 HBM-traffic summary of the dominant kernel of each workload

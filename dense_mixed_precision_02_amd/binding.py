@@ -9,7 +9,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libdmp_gemm.so"
 
 GEMM_F16, GEMM_BF16, GEMM_I8, GEMM_F64 = 0, 1, 2, 3
-GEMM_A_COLMAJOR, GEMM_B_COLMAJOR = 1, 2
+GEMM_A_COLMAJOR, GEMM_B_COLMAJOR, GEMM_A_SHARED, GEMM_B_SHARED = 1, 2, 4, 8
 GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32, GEMM_OUT_F64 = 0, 1, 2, 3, 4
 GEMM_OK = 0
 
@@ -175,19 +175,22 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
     if dt is None or B.dtype != A.dtype:
         raise TypeError("A and B must both be float16, bfloat16, int8 or float64")
     acc = {GEMM_I8: torch.int32, GEMM_F64: torch.float64}.get(dt, torch.float32)
-    if A.dim() != B.dim() or A.dim() not in (2, 3):
-        raise ValueError("A and B must both be 2-D or both 3-D")
+    if A.dim() not in (2, 3) or B.dim() not in (2, 3):
+        raise ValueError("A and B must be 2-D or 3-D")
     if not (A.is_cuda and B.is_cuda):
         raise ValueError("tensors must be on the GPU")
     M, K = A.shape[-2], A.shape[-1]
     N = B.shape[-1]
-    batch = A.shape[0] if A.dim() == 3 else 1
-    if B.shape[-2] != K or (A.dim() == 3 and B.shape[0] != batch):
+    nd = max(A.dim(), B.dim())
+    batch = A.shape[0] if A.dim() == 3 else (B.shape[0] if B.dim() == 3 else 1)
+    a_shared = A.dim() == 2 and nd == 3
+    b_shared = B.dim() == 2 and nd == 3
+    if B.shape[-2] != K or (A.dim() == 3 and B.dim() == 3 and B.shape[0] != batch):
         raise ValueError("shape mismatch between A and B")
     if C is None:
         beta = 0.0
     else:
-        if not C.is_cuda or C.dim() != A.dim() or C.shape[-2:] != (M, N):
+        if not C.is_cuda or C.dim() != nd or C.shape[-2:] != (M, N):
             raise ValueError("C must be a GPU tensor of shape (..., M, N)")
         if C.stride(-1) != 1:
             raise ValueError("C must be row-major")
@@ -200,13 +203,13 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
         raise TypeError("out dtype must be float32, float16, bfloat16 or int32")
     a_col, lda = _operand_layout(A, M, K, "A")
     b_col, ldb = _operand_layout(B, K, N, "B")
-    shape = (batch, M, N) if A.dim() == 3 else (M, N)
+    shape = (batch, M, N) if nd == 3 else (M, N)
     if C is not None:
         ldc = max(C.stride(-2), N, 1)
         strides = C.stride()
     else:
         ldc = max(N, 1)
-        strides = (M * ldc, ldc, 1) if A.dim() == 3 else (ldc, 1)
+        strides = (M * ldc, ldc, 1) if nd == 3 else (ldc, 1)
     if out is None:
         out = torch.empty_strided(shape, strides, dtype=d_dtype, device=A.device)
     if tuple(out.shape) != shape or out.stride() != strides:
@@ -214,9 +217,11 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
     if batch > 1:
         want_a = (K if a_col else M) * lda
         want_b = (N if b_col else K) * ldb
-        if A.stride(0) != want_a or B.stride(0) != want_b or out.stride(0) != M * ldc:
+        if (not a_shared and A.stride(0) != want_a) or (not b_shared and B.stride(0) != want_b) \
+                or out.stride(0) != M * ldc:
             raise ValueError("batched operands must have contiguous batch strides")
-    flags = (GEMM_A_COLMAJOR if a_col else 0) | (GEMM_B_COLMAJOR if b_col else 0)
+    flags = (GEMM_A_COLMAJOR if a_col else 0) | (GEMM_B_COLMAJOR if b_col else 0) | \
+        (GEMM_A_SHARED if a_shared else 0) | (GEMM_B_SHARED if b_shared else 0)
     h = handle if handle is not None else default_handle()
     stream = torch.cuda.current_stream(A.device).cuda_stream
     h.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, out.data_ptr(),

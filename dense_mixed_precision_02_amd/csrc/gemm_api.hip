@@ -12,6 +12,7 @@
 #include "aux_kernels.hpp"
 #include "dgemm.hpp"
 #include "tile_gemm.hpp"
+#include "tiny_gemm.hpp"
 
 using namespace dmp;
 
@@ -27,7 +28,8 @@ namespace {
 // Workgroup tile shapes of the tiled kernel (4 waves each, 2 x 2); the fp64
 // kernels have their own.
 enum Cfg { CFG_L = 0, CFG_M = 1, CFG_S = 2, CFG_GENERIC = 3, CFG_D128 = 4, CFG_D64 = 5,
-           CFG_DGENERIC = 6 };
+           CFG_DGENERIC = 6, CFG_TINY4 = 7, CFG_TINY16 = 8 };
+constexpr unsigned ALL_FLAGS = GEMM_A_COLMAJOR | GEMM_B_COLMAJOR | GEMM_A_SHARED | GEMM_B_SHARED;
 constexpr int CFG_EDGE[3] = {256, 128, 64};
 
 struct Plan {
@@ -67,7 +69,7 @@ int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const
     if (!h) return GEMM_ERR_INVALID_ARG;
     if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8 && dtype != GEMM_F64)
         return GEMM_ERR_INVALID_ARG;
-    if (flags & ~(unsigned)(GEMM_A_COLMAJOR | GEMM_B_COLMAJOR)) return GEMM_ERR_INVALID_ARG;
+    if (flags & ~ALL_FLAGS) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
     // output stage: fp16/bf16 inputs take fp32/fp16/bf16 C and D and any alpha,
     // beta; int8 and fp64 inputs keep C and D in their accumulator type, with
@@ -163,6 +165,14 @@ Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, in
         return P;
     }
     if (dtype == GEMM_F64) return make_plan_f64(h, A, B, M, N, K, lda, ldb, a_col, b_col, batch, check_ptrs);
+    if (M <= 16 && N <= 16) {
+        // tiny products: several problems per multi-block instruction
+        const int nb = (M <= 4 && N <= 4) ? 16 : 4;
+        P.cfg = nb == 16 ? CFG_TINY4 : CFG_TINY16;
+        P.tiles_m = P.tiles_n = 1;
+        P.grid = cdiv(batch, 4 * nb);
+        return P;
+    }
     const int es = elem_size(dtype);
     const int64_t kt = 128 / es;
     if (!granule_ok(A, B, M, N, K, lda, ldb, dtype, a_col, b_col, check_ptrs)) {
@@ -224,6 +234,8 @@ const char *cfg_name(int cfg) {
     case CFG_D128: return "dtile128x128";
     case CFG_D64: return "dtile64x64";
     case CFG_DGENERIC: return "dgeneric16x16";
+    case CFG_TINY4: return "tiny4x4x16b";
+    case CFG_TINY16: return "tiny16x16x4b";
     default: return "generic32x32";
     }
 }
@@ -319,6 +331,55 @@ hipError_t launch_reduce(int dtype, const void *W, const void *C, void *D, int64
     return launch_reduce_t<float>(W, C, D, M, N, ldc, batch, S, ep, s);
 }
 
+template <class DT, int S>
+hipError_t launch_tiny_t(const TinyArgs &a, bool sa, bool sb, int64_t grid, hipStream_t s) {
+    const dim3 g((unsigned)grid), blk(256);
+    if (!sa && !sb) hipLaunchKernelGGL((tiny_gemm<DT, S, false, false>), g, blk, 0, s, a);
+    else if (sa && !sb) hipLaunchKernelGGL((tiny_gemm<DT, S, true, false>), g, blk, 0, s, a);
+    else if (!sa && sb) hipLaunchKernelGGL((tiny_gemm<DT, S, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((tiny_gemm<DT, S, true, true>), g, blk, 0, s, a);
+    return hipGetLastError();
+}
+
+template <class DT>
+hipError_t launch_tiny_dt(int cfg, const TinyArgs &a, bool sa, bool sb, int64_t grid, hipStream_t s) {
+    return cfg == CFG_TINY4 ? launch_tiny_t<DT, 4>(a, sa, sb, grid, s)
+                            : launch_tiny_t<DT, 16>(a, sa, sb, grid, s);
+}
+
+// Tiny-product launch: four consecutive k of a K-contiguous operand row are
+// loaded as one access when every row start is aligned to four elements.
+hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, const void *C,
+                       void *D, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                       int64_t ldc, bool a_col, bool b_col, int64_t sA, int64_t sB, int64_t sC,
+                       int64_t batch, const EpiParams &ep, bool sa, bool sb, hipStream_t s) {
+    TinyArgs t;
+    t.A = A; t.B = B; t.C = C; t.D = D;
+    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldb; t.ldc = ldc;
+    t.sA = sA; t.sB = sB; t.sC = sC; t.batch = batch;
+    t.a_col = a_col; t.b_col = b_col;
+    const uintptr_t es = (uintptr_t)elem_size(dtype);
+    t.a_vec = !a_col && lda % 4 == 0 && sA % 4 == 0 && (uintptr_t)A % (4 * es) == 0;
+    t.b_vec = b_col && ldb % 4 == 0 && sB % 4 == 0 && (uintptr_t)B % (4 * es) == 0;
+    // LDS staging of a wave's operand region: 16-byte aligned starts, and the
+    // region of NB problems (up to the last element of the last one) fits
+    const int64_t nb = P.cfg == CFG_TINY4 ? 16 : 4;
+    t.ext_a = a_col ? (K - 1) * lda + M : (M - 1) * lda + K;
+    t.ext_b = b_col ? (N - 1) * ldb + K : (K - 1) * ldb + N;
+    t.stage_a = !sa && (uintptr_t)A % 16 == 0 && (sA * (int64_t)es) % 16 == 0 &&
+                ((nb - 1) * sA + t.ext_a) * (int64_t)es <= TINY_STAGE;
+    t.stage_b = !sb && (uintptr_t)B % 16 == 0 && (sB * (int64_t)es) % 16 == 0 &&
+                ((nb - 1) * sB + t.ext_b) * (int64_t)es <= TINY_STAGE;
+    const int acc_ty = acc_type(dtype);
+    t.flat_out = ldc == N && ep.d_type == acc_ty && (!ep.use_c || ep.c_type == acc_ty) &&
+                 (uintptr_t)D % 16 == 0 && (!ep.use_c || (uintptr_t)C % 16 == 0) &&
+                 (sC * 4) % 16 == 0 && nb * sC * 4 <= TINY_OUT;
+    t.ep = ep;
+    if (dtype == GEMM_F16) return launch_tiny_dt<F16>(P.cfg, t, sa, sb, P.grid, s);
+    if (dtype == GEMM_BF16) return launch_tiny_dt<BF16>(P.cfg, t, sa, sb, P.grid, s);
+    return launch_tiny_dt<I8>(P.cfg, t, sa, sb, P.grid, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -404,12 +465,20 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
     hipStream_t s = (hipStream_t)stream;
     const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
-    const int64_t sA = (a_col ? K : M) * lda, sB = (b_col ? N : K) * ldb, sC = M * ldc;
+    const bool a_sh = flags & GEMM_A_SHARED, b_sh = flags & GEMM_B_SHARED;
+    const int64_t sA = a_sh ? 0 : (a_col ? K : M) * lda, sB = b_sh ? 0 : (b_col ? N : K) * ldb;
+    const int64_t sC = M * ldc;
     const Plan P = make_plan(h, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
     if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
 
     if (P.copy_only)
         return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, ep, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+
+    if (P.cfg == CFG_TINY4 || P.cfg == CFG_TINY16)
+        return launch_tiny(P, dtype, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
+                           batch, ep, a_sh, b_sh, s) == hipSuccess
                    ? GEMM_OK
                    : GEMM_ERR_HIP;
 

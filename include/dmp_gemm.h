@@ -35,7 +35,14 @@
  *   B col-major (GEMM_B_COLMAJOR): B[k][j] at B[k + j*ldb], ldb >= K
  *   C and D are row-major and share ldc >= N: X[i][j] at X[i*ldc + j]
  *   Batches are contiguous: A_b = A + b*(row-major ? M : K)*lda,
- *   B_b = B + b*(row-major ? K : N)*ldb, C_b = C + b*M*ldc, D_b = D + b*M*ldc.
+ *   B_b = B + b*(row-major ? K : N)*ldb, C_b = C + b*M*ldc, D_b = D + b*M*ldc;
+ *   with GEMM_A_SHARED (GEMM_B_SHARED) A_b = A (B_b = B) for every b.
+ *
+ * Products with M <= 16 and N <= 16 (fp16, bf16, int8) run on the multi-block
+ * matrix instructions, several batch entries per instruction (pages: "CDNA2
+ * dense MFMA builtins", section "Accumulator layout", 4x4 and 16x16 shapes);
+ * a shared A or B is then loaded once and broadcast by the instruction's
+ * cbsz/abid and blgp modifiers ("MFMA common parameters").
  *
  * Ownership: the caller allocates A, B, C and D in device memory and keeps them
  * alive until the work on `stream` has finished.  The library never frees caller
@@ -63,8 +70,13 @@ typedef struct gemm_handle *gemm_handle_t;
 
 typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_I8 = 2, GEMM_F64 = 3 } gemm_dtype_t;
 
-/* flags: bitwise OR; default (0) is row-major A and row-major B. */
-enum { GEMM_A_COLMAJOR = 1u, GEMM_B_COLMAJOR = 2u };
+/*
+ * flags: bitwise OR; default (0) is row-major A and row-major B, each with its
+ * own matrix per batch entry.  GEMM_A_SHARED / GEMM_B_SHARED: one A (B) serves
+ * every batch entry (batch stride 0), e.g. one small transform applied to many
+ * inputs.
+ */
+enum { GEMM_A_COLMAJOR = 1u, GEMM_B_COLMAJOR = 2u, GEMM_A_SHARED = 4u, GEMM_B_SHARED = 8u };
 
 typedef enum {
     GEMM_OK = 0,

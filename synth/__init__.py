@@ -150,6 +150,10 @@ CONFIGS = {
     # uniform[-1,1], C fp64 uniform[-1,1]
     "F1": dict(dtype="f64", M=4096, N=4096, K=4096, seed=7, ab_dist="uniform",
                ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
+    # tiny products (the multi-block instructions): 2^20 independent 4x4x16 fp16
+    # problems, A/B row-major uniform[-1,1], C fp32 uniform[-1,1]
+    "T1": dict(dtype="f16", M=4, N=4, K=16, batch=1 << 20, seed=8, ab_dist="uniform",
+               ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
 }
 
 CONFIG_LABELS = {
@@ -160,6 +164,7 @@ CONFIG_LABELS = {
     "C5": "gemm 1024x1024x65536 bf16 (row-major), C fp32 zeros",
     "S1": "gemm 4096x4096x4096 fp16 (row-major), C fp32",
     "F1": "gemm 4096x4096x4096 fp64 (row-major), C fp64",
+    "T1": "batched gemm 1048576 x 4x4x16 fp16 (row-major), C fp32",
 }
 
 

@@ -64,7 +64,7 @@ def plan_status(*args):
     (4, 6, 8, 8, 6, 5, 0, 0, 1),           # ldc < N
     (4, 4, 8, 8, 4, 4, 5, 0, 1),           # bad dtype
     (4, 4, 8, 8, 4, 4, -1, 0, 1),          # bad dtype
-    (4, 4, 8, 8, 4, 4, 0, 4, 1),           # unknown flag bit
+    (4, 4, 8, 8, 4, 4, 0, 16, 1),          # unknown flag bit
     (4, 4, 8, 8, 4, 4, 0, 0, -1),          # negative batch
 ])
 def test_validation_rejects(args):
@@ -124,3 +124,18 @@ def test_f64_plans():
     assert dmp.plan_label(64, 64, 31, 64, 64, 64, dmp.GEMM_F64,
                           dmp.GEMM_A_COLMAJOR).startswith("dtile64x64")
     assert plan_status(4, 4, 0, 1, 4, 4, dmp.GEMM_F64, 0, 1) == (0, "copy_c k=0")
+
+
+def test_tiny_plans():
+    # 2^20 independent 4x4x16 fp16 products: 16 per instruction, 64 per workgroup
+    assert dmp.plan_label(4, 4, 16, 16, 4, 4, dmp.GEMM_F16, 0, 1 << 20) == \
+        "tiny4x4x16b f16 a:row b:row splitk=1 grid=16384"
+    assert dmp.plan_label(16, 16, 16, 16, 16, 16, dmp.GEMM_BF16, 0, 1000).startswith("tiny16x16x4b")
+    assert dmp.plan_label(5, 3, 7, 7, 3, 3, dmp.GEMM_I8).startswith("tiny16x16x4b")
+    # shared operands are accepted on every path
+    for fl in (dmp.GEMM_A_SHARED, dmp.GEMM_B_SHARED, dmp.GEMM_A_SHARED | dmp.GEMM_B_SHARED):
+        assert plan_status(4, 4, 16, 16, 4, 4, 0, fl, 100)[0] == 0
+        assert plan_status(512, 512, 512, 512, 512, 512, 0, fl, 4)[0] == 0
+    # fp64 keeps its own kernels
+    assert dmp.plan_label(4, 4, 16, 16, 4, 4, dmp.GEMM_F64, 0, 100).startswith("dgeneric") or \
+        dmp.plan_label(4, 4, 16, 16, 4, 4, dmp.GEMM_F64, 0, 100).startswith("dtile")

@@ -175,7 +175,7 @@ def test_invalid_arguments_enqueue_nothing(handle):
     A = torch.zeros(8, 8, dtype=torch.int16, device="cuda")
     bad = [
         dict(M=-1), dict(K=-1), dict(lda=7), dict(ldb=7), dict(ldc=7), dict(dtype=5),
-        dict(flags=8), dict(batch=-1), dict(Aptr=0), dict(Cptr=0), dict(Dptr=0),
+        dict(flags=16), dict(batch=-1), dict(Aptr=0), dict(Cptr=0), dict(Dptr=0),
         dict(Cptr=C.data_ptr() + 2),
     ]
     for b in bad:
