@@ -179,6 +179,40 @@ def gemm_points(dtype: str, A, B, C, pts: np.ndarray, M: int, N: int, K: int,
     return Di if dtype == "i8" else (D, S)
 
 
+def prune24(dtype: str, A: np.ndarray, M: int, K: int, lda: int, batch: int = 1) -> np.ndarray:
+    """2:4 structured pruning of a row-major A (the form the sparse matrix
+    instructions consume; pages: "MFMA common parameters", sparse parameter idx:
+    two of every four consecutive K positions hold the non-zeros).  In every
+    group of four consecutive k of a row (the last group may be shorter) the two
+    entries of largest magnitude are kept -- on a tie the lower k -- and the
+    others set to zero.  Returns a copy of A's storage with the dropped entries
+    replaced by +0; kept entries keep their exact bit patterns."""
+    out = np.array(A, copy=True)
+    if dtype in ("f16", "bf16"):
+        table = decode(dtype, np.arange(65536, dtype=np.uint32).astype(np.uint16))
+        mag = np.abs(table[np.asarray(A, dtype=np.uint16)])
+    else:
+        mag = np.abs(np.asarray(A, dtype=np.float64))
+    mag = mag.reshape(A.shape)[:batch, :M, :K]
+    Kp = (K + 3) // 4 * 4
+    # absent positions of a short last group never beat anything
+    m = np.full((batch, M, Kp), -1.0)
+    m[:, :, :K] = mag
+    g = m.reshape(batch, M, Kp // 4, 4)
+    # entry x is beaten by y (same group) if |y| > |x|, or |y| == |x| and y comes first
+    beaten = np.zeros(g.shape, dtype=np.int64)
+    for x in range(4):
+        for y in range(4):
+            if y == x:
+                continue
+            beats = (g[..., y] > g[..., x]) | ((g[..., y] == g[..., x]) & (y < x))
+            beaten[..., x] += beats
+    keep = (beaten < 2).reshape(batch, M, Kp)[:, :, :K]
+    region = out[:batch, :M, :K]
+    region[~keep] = 0
+    return out
+
+
 def _f64_args(A, B, C):
     for x in (A, B, C):
         assert x.dtype == np.float64 and x.flags["C_CONTIGUOUS"], "fp64 operands are float64"

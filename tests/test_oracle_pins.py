@@ -530,3 +530,53 @@ def test_f64_tolerance_accepts_fp64_sum_and_rejects_dropped_term():
     assert np.all(oracle.f64_error(seq, Dh[0], Dl[0]) <= tol)
     dropped = seq - np.outer(A[:, 100], B[100, :])
     assert np.any(oracle.f64_error(dropped, Dh[0], Dl[0]) > tol)
+
+
+# ------------------------------------------------------------ 2:4 pruning
+
+def test_prune24_hand_example():
+    vals = np.array([[0.5, -2.0, 1.0, 0.25, 3.0, 3.0, -3.0, 1.0, 0.0, 0.0, 0.0, 7.0, 1.0, -1.0]])
+    A = synth.f64_to_f16_bits(vals)[None].copy()
+    P = oracle.prune24("f16", A, M=1, K=14, lda=14)
+    got = P[0].view(np.float16).astype(np.float64)
+    # groups: {0.5,-2,1,0.25} keep -2, 1; {3,3,-3,1} ties keep the first two 3s;
+    # {0,0,0,7} keep 7 and the first 0; short group {1,-1}: both kept
+    want = np.array([[0, -2.0, 1.0, 0, 3.0, 3.0, 0, 0, 0.0, 0, 0, 7.0, 1.0, -1.0]])
+    assert np.array_equal(got, want)
+
+
+def test_prune24_brute_force_and_properties():
+    rng = np.random.default_rng(12)
+    for dtype in ("f16", "bf16"):
+        p = synth.make_problem(dtype, 9, 3, 37, batch=2, pad=3, seed=13)
+        # many exact ties: values from a small set
+        if dtype == "f16":
+            p.A = synth.f64_to_f16_bits(rng.choice([-2.0, -1.0, 0.0, 1.0, 2.0, 0.5], size=p.A.shape))
+        P = oracle.prune24(dtype, p.A, M=p.M, K=p.K, lda=p.lda, batch=2)
+        va, vp = lib_decode(dtype, p.A), lib_decode(dtype, P)
+        for b in range(2):
+            for i in range(p.M):
+                for g in range(0, p.K, 4):
+                    ks = list(range(g, min(g + 4, p.K)))
+
+                    def beats(x, y):  # x is preferred to y: larger magnitude, else lower k
+                        return abs(va[b, i, x]) > abs(va[b, i, y]) or \
+                            (abs(va[b, i, x]) == abs(va[b, i, y]) and x < y)
+                    # brute force over all candidate pairs: the one whose members
+                    # beat every other member of the group
+                    cands = [set(x) for x in itertools.combinations(ks, min(2, len(ks)))
+                             if all(beats(u, w) for u in x for w in ks if w not in x)]
+                    assert len(cands) == 1
+                    keep = cands[0]
+                    for k in ks:
+                        if k in keep:
+                            assert P[b, i, k] == p.A[b, i, k]      # exact bits
+                        else:
+                            assert vp[b, i, k] == 0
+                    assert sum(1 for k in ks if vp[b, i, k] != 0) <= 2
+                    dropped = [abs(va[b, i, k]) for k in ks if k not in keep]
+                    assert all(abs(va[b, i, k]) >= max(dropped, default=0) for k in keep)
+            # padding columns untouched
+            assert np.array_equal(P[b, :, p.K:], p.A[b, :, p.K:])
+        # idempotent, and a 2:4 matrix is its own pruning
+        assert np.array_equal(oracle.prune24(dtype, P, M=p.M, K=p.K, lda=p.lda, batch=2), P)
