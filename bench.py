@@ -28,6 +28,9 @@ sys.path.insert(0, ROOT)
 # Published MI355X dense peaks (256 CUs x 2.4 GHz): fp16/bf16 4096 FLOP/clk/CU,
 # int8 8192 OP/clk/CU, fp64 matrix 128 FLOP/clk/CU; HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f64": 78.6}
+# the sparse instructions do the dense-equivalent work of a 2:4 A at twice the dense rate
+SPARSE_PEAK_TFLOPS = 5033.2
+SPARSE_CONFIGS = {"SP1"}
 PEAK_HBM_GBS = 8000.0
 DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # Configs whose bounding roof is HBM rather than the matrix cores (arithmetic
@@ -109,7 +112,7 @@ def cpu_baseline(p, budget_s: float = 15.0):
             "sample": f"{what} of the same seeded problem ({fl / 2:.3g} MACs, {dt:.1f} s)"}
 
 
-def parity_sample(p, D_host, ex=None):
+def parity_sample(p, D_host, ex=None, sparse=False):
     """Oracle check of the benchmarked output at sampled positions (not timed)."""
     import numpy as np
 
@@ -128,6 +131,12 @@ def parity_sample(p, D_host, ex=None):
              if c_type != "none" else np.zeros(n))
         Dref = oracle.scaled_reference(P, c, alpha, beta)
         tol = oracle.scaled_tolerance(p.K, S, c, Dref, alpha, beta, d_type)
+        ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+        return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
+    if sparse:
+        pruned = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch)
+        Dref, S = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **p.oracle_args())
+        tol = oracle.float_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
         ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     if p.dtype == "f64":
@@ -193,6 +202,7 @@ def main():
         return t.to(dev)
 
     ex = None
+    sparse = name in SPARSE_CONFIGS
     A, B = up(p.A), up(p.B)
     if args.d_type is not None:
         if p.dtype == "i8":
@@ -210,11 +220,33 @@ def main():
     flags = (dmp.GEMM_A_COLMAJOR if p.a_col else 0) | (dmp.GEMM_B_COLMAJOR if p.b_col else 0)
     code = DTYPE_CODE[p.dtype]
     label = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch, handle=h)
+    if name in SPARSE_CONFIGS:
+        label = f"sparse24 smfmac32x32x32 tile256x256 grid={-(-p.M // 256) * -(-p.N // 256) * p.batch}"
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     args_run = (A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, D.data_ptr(),
                 p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch)
-    if ex is None:
+    prune_us = None
+    if sparse:
+        kp = dmp.sparse24_kp(p.K)
+        Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int16, device=dev)
+        meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device=dev)
+        # the compression is a one-off preparation of A, timed on its own
+        q0 = torch.cuda.Event(enable_timing=True)
+        q1 = torch.cuda.Event(enable_timing=True)
+        q0.record(stream)
+        rc = h.prune24(A.data_ptr(), p.M, p.K, p.lda, code, p.batch, Ac.data_ptr(), meta.data_ptr(),
+                       sp)
+        q1.record(stream)
+        torch.cuda.synchronize()
+        assert rc == 0, rc
+        prune_us = q0.elapsed_time(q1) * 1e3
+
+        def step():
+            rc2 = h.run_sparse24(Ac.data_ptr(), meta.data_ptr(), B.data_ptr(), C.data_ptr(),
+                                 D.data_ptr(), p.M, p.N, p.K, p.ldb, p.ldc, code, flags, p.batch, sp)
+            assert rc2 == 0, rc2
+    elif ex is None:
         def step():
             h.run(*args_run, sp)
     else:
@@ -243,7 +275,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     D_host = D.cpu().numpy()
 
-    peak = PEAK_TFLOPS[p.dtype]
+    peak = SPARSE_PEAK_TFLOPS if sparse else PEAK_TFLOPS[p.dtype]
     unit = "TOP/s" if p.dtype == "i8" else "TFLOP/s"
     nbytes = algorithmic_bytes(p, *(ex[:2] if ex else (None, None)))
     if name in HBM_BOUND:
@@ -278,8 +310,12 @@ def main():
                    "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
                    "timed_wall_s": round(wall, 3)},
         "roofline": roof,
-        "parity": parity_sample(p, D_host, ex),
+        "parity": parity_sample(p, D_host, ex, sparse),
     }
+    if sparse:
+        line["config"]["prune_us"] = round(prune_us, 1)
+        line["config"]["note"] = ("value = 2*M*N*K / time, the dense-equivalent rate of the 2:4 "
+                                  "product; peak = the sparse instructions' rate (2x dense)")
     if ex is not None:
         line["config"]["output_stage"] = {"c_type": ex[0], "d_type": ex[1], "alpha": ex[2],
                                           "beta": ex[3]}

@@ -13,8 +13,8 @@ GEMM_A_COLMAJOR, GEMM_B_COLMAJOR, GEMM_A_SHARED, GEMM_B_SHARED = 1, 2, 4, 8
 GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32, GEMM_OUT_F64 = 0, 1, 2, 3, 4
 GEMM_OK = 0
 
-EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_destroy",
-                    "gemm_status_string", "gemm_plan")
+EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_prune24",
+                    "gemm_run_sparse24", "gemm_destroy", "gemm_status_string", "gemm_plan")
 
 _lib = None
 _lock = threading.Lock()
@@ -55,6 +55,11 @@ def load_library():
         lib.gemm_run_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, ctypes.c_uint, i64, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        lib.gemm_prune24.restype = ctypes.c_int
+        lib.gemm_prune24.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, i64, vp, vp, vp]
+        lib.gemm_run_sparse24.restype = ctypes.c_int
+        lib.gemm_run_sparse24.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                          ctypes.c_int, ctypes.c_uint, i64, vp]
         lib.gemm_plan.restype = ctypes.c_int
         lib.gemm_plan.argtypes = [vp, i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_uint,
                                   i64, ctypes.c_char_p, ctypes.c_size_t]
@@ -121,6 +126,16 @@ class Handle:
         return load_library().gemm_run_ex(self.ptr, A, B, C, D, M, N, K, lda, ldb, ldc, dtype,
                                           flags, batch, alpha, beta, c_type, d_type, stream)
 
+    def prune24(self, A, M, K, lda, dtype, batch, Ac, meta, stream=0) -> int:
+        """Raw-pointer call of gemm_prune24; returns the status code."""
+        return load_library().gemm_prune24(self.ptr, A, M, K, lda, dtype, batch, Ac, meta, stream)
+
+    def run_sparse24(self, Ac, meta, B, C, D, M, N, K, ldb, ldc, dtype, flags=0, batch=1,
+                     stream=0) -> int:
+        """Raw-pointer call of gemm_run_sparse24; returns the status code."""
+        return load_library().gemm_run_sparse24(self.ptr, Ac, meta, B, C, D, M, N, K, ldb, ldc,
+                                                dtype, flags, batch, stream)
+
     def run_ex(self, *args, **kw) -> None:
         """Like status_ex() but raises on a non-zero status."""
         rc = self.status_ex(*args, **kw)
@@ -129,6 +144,11 @@ class Handle:
 
 
 _default = {}
+
+
+def sparse24_kp(K: int) -> int:
+    """Dense k per compressed row: 64 * ceil(K / 64) (Kp/2 values, Kp/16 index words)."""
+    return -(-K // 64) * 64
 
 
 def default_handle() -> Handle:

@@ -96,6 +96,20 @@ __device__ static inline void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+// Workgroup barrier after this wave's LDS reads have completed and at most n of
+// its vector-memory operations are outstanding.  Unlike __syncthreads() it does
+// not wait for every outstanding global load, so copies for later k-tiles stay in
+// flight; the empty asm statements keep the compiler from moving memory
+// accesses across it.
+template <int n>
+__device__ static inline void barrier_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // C is added once after the reduction: an fp32 round-to-nearest-even add, or an
 // int32 add that wraps modulo 2^32 (done in unsigned arithmetic, where wrapping
 // is defined).

@@ -11,6 +11,7 @@
 #include "../../include/dmp_gemm.h"
 #include "aux_kernels.hpp"
 #include "dgemm.hpp"
+#include "sparse_gemm.hpp"
 #include "tile_gemm.hpp"
 #include "tiny_gemm.hpp"
 
@@ -380,6 +381,22 @@ hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, c
     return launch_tiny_dt<I8>(P.cfg, t, sa, sb, P.grid, s);
 }
 
+// Compressed-A geometry: Kp = 64 * ceil(K / 64) dense k, Kp/2 values and
+// Kp/16 index words per row.
+int64_t sparse_kp(int64_t K) { return cdiv(K, 64) * 64; }
+
+int validate_sparse(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int64_t batch) {
+    if (!h) return GEMM_ERR_INVALID_ARG;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
+    if (M > (1ll << 31) - 1024 || N > (1ll << 31) - 1024 || K > (1ll << 31) - 1024 ||
+        batch > (1ll << 30))
+        return GEMM_ERR_INVALID_ARG;
+    // byte offsets inside one 256-row panel of the compressed operand fit 31 bits
+    if (256 * (sparse_kp(K) / 2) * 2 >= (1ll << 31) - (1ll << 22)) return GEMM_ERR_INVALID_ARG;
+    return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -541,6 +558,70 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
     if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, ep, s) != hipSuccess)
         return GEMM_ERR_HIP;
     return GEMM_OK;
+}
+
+int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t lda, int dtype,
+                 int64_t batch, void *Ac, void *meta, void *stream) {
+    int rc = validate_sparse(h, M, 1, K, dtype, batch);
+    if (rc != GEMM_OK) return rc;
+    if (K > 0 && lda < K) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || batch == 0 || K == 0) return GEMM_OK;
+    if (!A || !Ac || !meta || (uintptr_t)A % 2 || (uintptr_t)Ac % 2 || (uintptr_t)meta % 2)
+        return GEMM_ERR_INVALID_ARG;
+    const int64_t kp = sparse_kp(K);
+    const int64_t items = batch * M * (kp / 16);
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(items, 256), 256 * 64));
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == GEMM_F16)
+        hipLaunchKernelGGL(prune24_kernel<F16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
+                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+    else
+        hipLaunchKernelGGL(prune24_kernel<BF16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
+                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const void *B,
+                      const void *C, void *D, int64_t M, int64_t N, int64_t K, int64_t ldb,
+                      int64_t ldc, int dtype, unsigned flags, int64_t batch, void *stream) {
+    int rc = validate_sparse(h, M, N, K, dtype, batch);
+    if (rc != GEMM_OK) return rc;
+    if (flags & ~(unsigned)GEMM_B_COLMAJOR) return GEMM_ERR_INVALID_ARG;
+    const bool b_col = flags & GEMM_B_COLMAJOR;
+    if (K > 0 && ldb < std::max<int64_t>(1, b_col ? K : N)) return GEMM_ERR_INVALID_ARG;
+    if (ldc < std::max<int64_t>(1, N)) return GEMM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    if (!C || !D || (uintptr_t)C % 4 || (uintptr_t)D % 4) return GEMM_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    const EpiParams ep = plain_epi(dtype);
+    if (K == 0)
+        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, ep, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+    // the operands go straight to LDS in 16-byte granules: aligned starts, whole
+    // granules along the contiguous extent of B, offsets within 31 bits
+    if (!Ac || !meta || !B || !aligned16(Ac) || !aligned16(meta) || !aligned16(B) || (ldb * 2) % 16 ||
+        (b_col ? K % 8 : N % 8) || (b_col ? 256 * ldb : 64 * ldb) * 2 >= (1ll << 31) - (1ll << 22))
+        return GEMM_ERR_INVALID_ARG;
+    const int64_t kp = sparse_kp(K);
+    SparseArgs a;
+    a.Ac = Ac; a.meta = meta; a.B = B; a.C = C; a.D = D;
+    a.M = M; a.N = N; a.K = K; a.ldac = kp / 2; a.ldm = kp / 16; a.ldb = ldb; a.ldc = ldc;
+    a.sAc = M * (kp / 2); a.sM = M * (kp / 16); a.sB = (b_col ? N : K) * ldb; a.sC = M * ldc;
+    a.tiles_m = (int)cdiv(M, 256); a.tiles_n = (int)cdiv(N, 256); a.batch = (int)batch;
+    a.nkt = (int)(kp / 64);
+    a.ep = ep;
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * batch;
+    if (grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
+    const dim3 g((unsigned)grid), blk(256);
+    if (dtype == GEMM_F16) {
+        if (b_col) hipLaunchKernelGGL((sparse_gemm<F16, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((sparse_gemm<F16, false>), g, blk, 0, s, a);
+    } else {
+        if (b_col) hipLaunchKernelGGL((sparse_gemm<BF16, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((sparse_gemm<BF16, false>), g, blk, 0, s, a);
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 int gemm_run(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,

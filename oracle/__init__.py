@@ -179,14 +179,16 @@ def gemm_points(dtype: str, A, B, C, pts: np.ndarray, M: int, N: int, K: int,
     return Di if dtype == "i8" else (D, S)
 
 
-def prune24(dtype: str, A: np.ndarray, M: int, K: int, lda: int, batch: int = 1) -> np.ndarray:
+def prune24(dtype: str, A: np.ndarray, M: int, K: int, lda: int, batch: int = 1,
+            return_keep: bool = False):
     """2:4 structured pruning of a row-major A (the form the sparse matrix
     instructions consume; pages: "MFMA common parameters", sparse parameter idx:
     two of every four consecutive K positions hold the non-zeros).  In every
     group of four consecutive k of a row (the last group may be shorter) the two
     entries of largest magnitude are kept -- on a tie the lower k -- and the
     others set to zero.  Returns a copy of A's storage with the dropped entries
-    replaced by +0; kept entries keep their exact bit patterns."""
+    replaced by +0; kept entries keep their exact bit patterns.  return_keep also
+    returns the (batch, M, K) mask of kept positions."""
     out = np.array(A, copy=True)
     if dtype in ("f16", "bf16"):
         table = decode(dtype, np.arange(65536, dtype=np.uint32).astype(np.uint16))
@@ -210,7 +212,7 @@ def prune24(dtype: str, A: np.ndarray, M: int, K: int, lda: int, batch: int = 1)
     keep = (beaten < 2).reshape(batch, M, Kp)[:, :, :K]
     region = out[:batch, :M, :K]
     region[~keep] = 0
-    return out
+    return (out, keep) if return_keep else out
 
 
 def _f64_args(A, B, C):

@@ -150,6 +150,10 @@ CONFIGS = {
     # uniform[-1,1], C fp64 uniform[-1,1]
     "F1": dict(dtype="f64", M=4096, N=4096, K=4096, seed=7, ab_dist="uniform",
                ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
+    # 2:4 structured-sparse A (the sparse instructions): the 4096^3 bf16 problem of
+    # C2 (A pruned on the GPU before the timed products), seed 9
+    "SP1": dict(dtype="bf16", M=4096, N=4096, K=4096, b_col=True, seed=9, ab_dist="normal",
+                c_dist="zeros"),
     # tiny products (the multi-block instructions): 2^20 independent 4x4x16 fp16
     # problems, A/B row-major uniform[-1,1], C fp32 uniform[-1,1]
     "T1": dict(dtype="f16", M=4, N=4, K=16, batch=1 << 20, seed=8, ab_dist="uniform",
@@ -165,6 +169,7 @@ CONFIG_LABELS = {
     "S1": "gemm 4096x4096x4096 fp16 (row-major), C fp32",
     "F1": "gemm 4096x4096x4096 fp64 (row-major), C fp64",
     "T1": "batched gemm 1048576 x 4x4x16 fp16 (row-major), C fp32",
+    "SP1": "gemm 4096x4096x4096 bf16, A 2:4-pruned (row-major), B col-major, C fp32 zeros",
 }
 
 

@@ -1,0 +1,180 @@
+"""GPU parity of the 2:4 structured-sparse path: the compressor against the
+oracle's pruning (values and index words bit for bit), and the sparse product
+against the dense oracle on the pruned A."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import DTYPE_CODE, log, sample_points
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def handle():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_mixed_precision_02_amd as dmp
+    h = dmp.Handle()
+    yield h
+    h.close()
+
+
+def kp_of(K):
+    return -(-K // 64) * 64
+
+
+def dev16(x):
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+
+
+def compress(handle, p, Ad=None):
+    """gemm_prune24 on p's A; returns device (Ac, meta)."""
+    kp = kp_of(p.K)
+    Ad = dev16(p.A) if Ad is None else Ad
+    Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int16, device="cuda")
+    meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device="cuda")
+    rc = handle.prune24(Ad.data_ptr(), p.M, p.K, p.lda, DTYPE_CODE[p.dtype], p.batch,
+                        Ac.data_ptr(), meta.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    return Ac, meta
+
+
+def expected_compressed(p):
+    """Ac and index words built from the oracle's kept positions."""
+    pruned, keep = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch, return_keep=True)
+    kp = kp_of(p.K)
+    keep_p = np.zeros((p.batch, p.M, kp), dtype=bool)
+    keep_p[:, :, :p.K] = keep
+    vals = np.zeros((p.batch, p.M, kp), dtype=np.uint16)
+    vals[:, :, :p.K] = p.A[:, :p.M, :p.K]
+    # groups with fewer than two present positions keep the lowest absent ones
+    g = keep_p.reshape(p.batch, p.M, kp // 4, 4)
+    for q in range(4):
+        need = g.sum(-1) < 2
+        g[..., q] |= need & ~g[..., q] & (np.arange(kp // 4)[None, None, :] * 4 + q >= p.K)
+    pos = np.argsort(~g, axis=-1, kind="stable")[..., :2]          # kept positions, ascending
+    v4 = vals.reshape(p.batch, p.M, kp // 4, 4)
+    Ac = np.take_along_axis(v4, pos, axis=-1).reshape(p.batch, p.M, kp // 2)
+    Ac = np.where(np.take_along_axis(g, pos, -1).reshape(Ac.shape), Ac, 0).astype(np.uint16)
+    bits = (pos[..., 0] | (pos[..., 1] << 2)).astype(np.uint32)    # 4 bits per group
+    w = bits.reshape(p.batch, p.M, kp // 16, 4)
+    meta = (w[..., 0] | (w[..., 1] << 4) | (w[..., 2] << 8) | (w[..., 3] << 12)).astype(np.uint16)
+    return pruned, Ac, meta
+
+
+def run_sparse(handle, p, Ac, meta, C=None, D=None):
+    B = dev16(p.B)
+    C = torch.from_numpy(p.C).cuda() if C is None else C
+    D = torch.empty_like(C) if D is None else D
+    rc = handle.run_sparse24(Ac.data_ptr(), meta.data_ptr(), B.data_ptr(), C.data_ptr(),
+                             D.data_ptr(), p.M, p.N, p.K, p.ldb, p.ldc, DTYPE_CODE[p.dtype],
+                             2 if p.b_col else 0, p.batch, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    return D.cpu().numpy()
+
+
+def check(p, pruned, Dg, exact=False, pts=None):
+    args = p.oracle_args()
+    Dg = Dg.reshape(p.batch, p.M, p.ldc)[:, :, :p.N]
+    if pts is not None:
+        ref, S = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **args)
+        got = Dg[pts[:, 0], pts[:, 1], pts[:, 2]].astype(np.float64)
+        c = p.C[pts[:, 0], pts[:, 1], pts[:, 2]]
+    else:
+        ref, S = oracle.gemm(p.dtype, pruned, p.B, p.C, **args)
+        got = Dg.astype(np.float64)
+        c = p.C[:, :p.M, :p.N]
+    if exact:
+        assert np.array_equal(got, ref)
+        return 0.0
+    tol = oracle.float_tolerance(p.K, S, c)
+    bad = np.argwhere(np.abs(got - ref) > tol)
+    assert bad.size == 0, f"{len(bad)} over the bound, first at {bad[0]}"
+    return float(np.max(np.abs(got - ref) / np.maximum(tol, 1e-300)))
+
+
+def test_workload_4096_cubed(handle):
+    p = synth.config_problem("SP1")
+    log(f"[sparse] {synth.CONFIG_LABELS['SP1']}")
+    Ac, meta = compress(handle, p)
+    pruned, eAc, emeta = expected_compressed(p)
+    assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc), "compressed values differ"
+    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta), "index words differ"
+    Dg = run_sparse(handle, p, Ac, meta)
+    r = check(p, pruned, Dg, pts=sample_points(p, 3000, seed=91))
+    log(f"[sparse] ok, max err/bound {r:.3g}")
+
+
+SHAPES = [(256, 256, 64), (300, 264, 200), (1, 8, 1000), (520, 136, 64 * 5), (256, 512, 4096 + 64),
+          (77, 40, 24)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_shapes_layouts(handle, dtype, b_col):
+    for n, (M, N, K) in enumerate(SHAPES):
+        if b_col and K % 8:
+            continue
+        for batch in (1, 3):
+            p = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=400 + n)
+            log(f"[sparse] {dtype} {batch} x {M}x{N}x{K} b_col={b_col}")
+            Ac, meta = compress(handle, p)
+            pruned, eAc, emeta = expected_compressed(p)
+            assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc)
+            assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+            check(p, pruned, run_sparse(handle, p, Ac, meta))
+            # exact-integer inputs: every partial sum an integer, so bit for bit
+            e = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=500 + n,
+                                   ab_dist="small_int", c_dist="small_int", c_range=(-8, 8))
+            Ac, meta = compress(handle, e)
+            pruned, _, _ = expected_compressed(e)
+            check(e, pruned, run_sparse(handle, e, Ac, meta), exact=True)
+
+
+def test_ties_padding_and_lda(handle):
+    """Tie-heavy values (many equal magnitudes, zeros), a padded lda, K not a
+    multiple of four."""
+    rng = np.random.default_rng(92)
+    p = synth.make_problem("f16", 130, 64, 203, seed=93)
+    # A with a padded leading dimension (B keeps whole 16-byte granules)
+    p.lda = p.K + 5
+    p.A = synth.f64_to_f16_bits(rng.choice([-1.0, 0.0, 1.0, 0.5, -0.5], size=(1, p.M, p.lda)))
+    Ac, meta = compress(handle, p)
+    pruned, eAc, emeta = expected_compressed(p)
+    assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+    check(p, pruned, run_sparse(handle, p, Ac, meta))
+
+
+def test_k_zero_alias_and_invalid(handle):
+    p = synth.make_problem("bf16", 64, 64, 0, seed=94)
+    C = torch.from_numpy(p.C).cuda()
+    D = torch.full_like(C, 5.0)
+    z = torch.zeros(16, dtype=torch.int16, device="cuda")
+    rc = handle.run_sparse24(z.data_ptr(), z.data_ptr(), z.data_ptr(), C.data_ptr(), D.data_ptr(),
+                             64, 64, 0, 64, 64, 1, 0, 1, 0)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.equal(D, C)
+    q = synth.make_problem("bf16", 256, 256, 128, seed=95)
+    Ac, meta = compress(handle, q)
+    pruned, _, _ = expected_compressed(q)
+    C = torch.from_numpy(q.C).cuda()
+    check(q, pruned, run_sparse(handle, q, Ac, meta, C=C, D=C))   # D aliases C
+    B = dev16(q.B)
+    D = torch.full_like(C, 3.0)
+    bad = [dict(dtype=2), dict(dtype=0, flags=1), dict(flags=4), dict(Bp=B.data_ptr() + 2),
+           dict(N=100), dict(ldb=260), dict(ldc=100), dict(Acp=Ac.data_ptr() + 2)]
+    for kw in bad:
+        a = dict(Acp=Ac.data_ptr(), Mp=meta.data_ptr(), Bp=B.data_ptr(), N=256, ldb=256, ldc=256,
+                 dtype=1, flags=0)
+        a.update(kw)
+        rc = handle.run_sparse24(a["Acp"], a["Mp"], a["Bp"], C.data_ptr(), D.data_ptr(), 256,
+                                 a["N"], 128, a["ldb"], a["ldc"], a["dtype"], a["flags"], 1, 0)
+        assert rc == 1, kw
+    torch.cuda.synchronize()
+    assert torch.all(D == 3.0)
