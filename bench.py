@@ -231,7 +231,11 @@ def main():
         kp = dmp.sparse24_kp(p.K)
         Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int16, device=dev)
         meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device=dev)
-        # the compression is a one-off preparation of A, timed on its own
+        # the compression is a one-off preparation of A, timed on its own (after
+        # one untimed call that loads the kernel)
+        rc = h.prune24(A.data_ptr(), p.M, p.K, p.lda, code, p.batch, Ac.data_ptr(), meta.data_ptr(),
+                       sp)
+        assert rc == 0, rc
         q0 = torch.cuda.Event(enable_timing=True)
         q1 = torch.cuda.Event(enable_timing=True)
         q0.record(stream)
