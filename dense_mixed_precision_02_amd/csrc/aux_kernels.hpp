@@ -118,4 +118,43 @@ __global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, co
     }
 }
 
+// Row-major int8 B (K x N, leading dimension ldb) to column-major form Bt
+// (Bt[j*ldt + k] = B[k*ldb + j], ldt a multiple of 16), per batch entry, in
+// 64 x 64 tiles through LDS: 16-byte row pieces in, 16-byte column pieces out.
+// The tiled GEMM reads a column-major B with plain 16-byte LDS reads where a
+// row-major one needs twice as many transposing reads.
+__global__ __launch_bounds__(256) void transpose_i8(const int8_t *B, int64_t K, int64_t N, int64_t ldb,
+                                                    int64_t sB, int8_t *Bt, int64_t ldt, int64_t sBt,
+                                                    int tiles_k, int tiles_n, int vec_in) {
+    __shared__ __attribute__((aligned(16))) uint8_t t[64][80];
+    const int tiles = tiles_k * tiles_n;
+    const int64_t b = blockIdx.x / tiles;
+    const int tile = blockIdx.x - (int)(b * tiles);
+    const int64_t k0 = (int64_t)(tile / tiles_n) * 64, n0 = (int64_t)(tile % tiles_n) * 64;
+    const int r = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 16;
+    const int8_t *src = B + b * sB + (k0 + r) * ldb + n0 + c0;
+    if (vec_in && k0 + r < K && n0 + c0 + 15 < N) {
+        *(intx4 *)&t[r][c0] = *(const intx4 *)src;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            t[r][c0 + e] = (k0 + r < K && n0 + c0 + e < N) ? (uint8_t)src[e] : (uint8_t)0;
+    }
+    __syncthreads();
+    const int j = threadIdx.x >> 2, kk = (threadIdx.x & 3) * 16;
+    if (n0 + j >= N) return;
+    int8_t *dst = Bt + b * sBt + (n0 + j) * ldt + k0 + kk;
+    intx4 v;
+    uint8_t *vb = (uint8_t *)&v;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) vb[e] = t[kk + e][j];
+    if (k0 + kk + 15 < K) {
+        *(intx4 *)dst = v;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (k0 + kk + e < K) dst[e] = (int8_t)vb[e];
+    }
+}
+
 }  // namespace dmp

@@ -41,6 +41,8 @@ struct Plan {
     int64_t grid = 0;
     bool reduce = false;     // second launch: fixed-order sum of partials + C
     bool copy_only = false;  // K == 0: D = C
+    bool transpose_b = false;  // int8 row-major B copied column-major into the workspace first
+    int64_t ldt = 0;           // its leading dimension
     size_t ws_needed = 0;
 };
 
@@ -176,7 +178,15 @@ Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, in
     }
     const int es = elem_size(dtype);
     const int64_t kt = 128 / es;
-    if (!granule_ok(A, B, M, N, K, lda, ldb, dtype, a_col, b_col, check_ptrs)) {
+    // int8 row-major B with a large M: a transposed copy (one pass over B into the
+    // workspace) lets the K loop use plain instead of transposing LDS reads; the
+    // copy is column-major with a 16-byte multiple leading dimension, so only A's
+    // granule conditions and K % 16 remain
+    const bool tb = dtype == GEMM_I8 && !b_col && (flags & GEMM_B_SHARED) == 0 && M >= 4096 &&
+                    K % 16 == 0;
+    const int64_t ldt = cdiv(K, 16) * 16;
+    if (tb ? !granule_ok(A, A, M, N, K, lda, ldt, dtype, a_col, true, check_ptrs)
+           : !granule_ok(A, B, M, N, K, lda, ldb, dtype, a_col, b_col, check_ptrs)) {
         P.cfg = CFG_GENERIC;
         P.tiles_m = (int)cdiv(M, 32);
         P.tiles_n = (int)cdiv(N, 32);
@@ -207,7 +217,7 @@ Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, in
         // least 8 k-tiles) so the large tile's low traffic per flop is kept;
         // a short K instead moves to smaller tiles.
         const int64_t s = std::min(cus / tiles(cfg), nkt / 8);
-        if (s >= 2) {
+        if (s >= 2 && !tb) {
             splits = s;
         } else {
             while (cfg < CFG_S && tiles(cfg) < cus && useful(cfg + 1) >= 0.75) ++cfg;
@@ -223,6 +233,10 @@ Plan make_plan(const gemm_handle *h, const void *A, const void *B, int64_t M, in
     if (P.splits > 1) {
         P.reduce = true;
         P.ws_needed = (size_t)P.splits * (size_t)batch * (size_t)M * (size_t)N * 4u;
+    } else if (tb) {
+        P.transpose_b = true;
+        P.ldt = ldt;
+        P.ws_needed = (size_t)batch * (size_t)N * (size_t)P.ldt;
     }
     return P;
 }
@@ -463,7 +477,8 @@ int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int
     }
     std::snprintf(label, label_len, "%s %s a:%s b:%s splitk=%d grid=%lld", cfg_name(P.cfg),
                   dtype_name(dtype), (flags & GEMM_A_COLMAJOR) ? "col" : "row",
-                  (flags & GEMM_B_COLMAJOR) ? "col" : "row", P.splits, (long long)P.grid);
+                  P.transpose_b ? "row->col" : (flags & GEMM_B_COLMAJOR) ? "col" : "row", P.splits,
+                  (long long)P.grid);
     return GEMM_OK;
 }
 
@@ -523,7 +538,7 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
         return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
     }
 
-    if (P.reduce && h->ws_bytes < P.ws_needed) {
+    if (P.ws_needed > h->ws_bytes) {
         int cur = 0;
         if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return GEMM_ERR_INVALID_ARG;
         if (h->ws) {
@@ -541,19 +556,36 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
         h->ws_bytes = P.ws_needed;
     }
 
+    const void *Bk = B;
+    int64_t ldbk = ldb, sBk = sB;
+    bool b_colk = b_col;
+    if (P.transpose_b) {
+        const int tk = (int)cdiv(K, 64), tn = (int)cdiv(N, 64);
+        const int64_t tgrid = (int64_t)tk * tn * batch;
+        if (tgrid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
+        const int vec_in = aligned16(B) && ldb % 16 == 0 && sB % 16 == 0;
+        hipLaunchKernelGGL(transpose_i8, dim3((unsigned)tgrid), dim3(256), 0, s, (const int8_t *)B, K,
+                           N, ldb, sB, (int8_t *)h->ws, P.ldt, N * P.ldt, tk, tn, vec_in);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+        Bk = h->ws;
+        ldbk = P.ldt;
+        sBk = N * P.ldt;
+        b_colk = true;
+    }
+
     TileArgs t;
-    t.A = A; t.B = B; t.C = C; t.D = D; t.W = h->ws;
-    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldb; t.ldc = ldc;
-    t.sA = sA; t.sB = sB; t.sC = sC;
+    t.A = A; t.B = Bk; t.C = C; t.D = D; t.W = h->ws;
+    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldbk; t.ldc = ldc;
+    t.sA = sA; t.sB = sBk; t.sC = sC;
     t.k_chunk = P.k_chunk;
     t.tiles_m = P.tiles_m; t.tiles_n = P.tiles_n;
     t.batch = (int)batch; t.splits = P.splits;
     t.partial = P.reduce ? 1 : 0;
     t.ep = ep;
     hipError_t e;
-    if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_col, P.grid, s);
-    else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_col, P.grid, s);
-    else e = launch_cfg<I8>(P.cfg, t, a_col, b_col, P.grid, s);
+    if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_colk, P.grid, s);
+    else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_colk, P.grid, s);
+    else e = launch_cfg<I8>(P.cfg, t, a_col, b_colk, P.grid, s);
     if (e != hipSuccess) return GEMM_ERR_HIP;
     if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, ep, s) != hipSuccess)
         return GEMM_ERR_HIP;

@@ -47,8 +47,10 @@
  * Ownership: the caller allocates A, B, C and D in device memory and keeps them
  * alive until the work on `stream` has finished.  The library never frees caller
  * memory.  A handle owns only a lazily grown device workspace (used by the
- * split-K path) and cached device properties; one handle serves one host thread
- * at a time.  D may alias C exactly (same pointer, same ldc); any other overlap
+ * split-K path and by the transposed copy of a row-major int8 B for large M)
+ * and cached device properties; one handle serves one host thread at a time,
+ * and calls through one handle on different streams must not overlap (they
+ * would share the workspace).  D may alias C exactly (same pointer, same ldc); any other overlap
  * between D and an input is undefined.
  *
  * Errors: every call returns a gemm_status_t.  Arguments are validated before

@@ -85,7 +85,7 @@ def test_plans_of_the_workloads():
                           dmp.GEMM_B_COLMAJOR) == "tile256x256 bf16 a:row b:col splitk=1 grid=256"
     # 8192^3 int8
     assert dmp.plan_label(8192, 8192, 8192, 8192, 8192, 8192, dmp.GEMM_I8) == \
-        "tile256x256 i8 a:row b:row splitk=1 grid=1024"
+        "tile256x256 i8 a:row b:row->col splitk=1 grid=1024"
     # skinny 1024 x 1024 x 65536: 16 tiles x 16 K-splits
     assert dmp.plan_label(1024, 1024, 65536, 65536, 1024, 1024, dmp.GEMM_BF16) == \
         "tile256x256 bf16 a:row b:row splitk=16 grid=256"

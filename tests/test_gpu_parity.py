@@ -232,3 +232,16 @@ def test_torch_front_end(handle):
     D8 = dmp.gemm(A8, B8, C8, out=C8)
     torch.cuda.synchronize()
     assert torch.equal(D8.cpu().long(), ref8)
+
+
+def test_int8_transposed_b_path(handle):
+    """Large-M int8 with row-major B goes through a transposed copy of B; ragged N and
+    K (multiples of 16) exercise the copy's edges, and a batch its batch stride."""
+    import dense_mixed_precision_02_amd as dmp
+    for (M, N, K, batch, pad) in [(4096, 520, 272, 1, 0), (4100, 96, 1040, 2, 16)]:
+        p = synth.make_problem("i8", M, N, K, batch=batch, pad=pad, seed=61,
+                               c_range=(-(1 << 20), 1 << 20))
+        lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, 2, 0, batch)
+        log(f"[i8-bT] {batch} x {M}x{N}x{K} pad={pad} {lbl}")
+        assert "row->col" in lbl
+        check_full(p, gpu_result(handle, p))
