@@ -120,40 +120,81 @@ __global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, co
 
 // Row-major int8 B (K x N, leading dimension ldb) to column-major form Bt
 // (Bt[j*ldt + k] = B[k*ldb + j], ldt a multiple of 16), per batch entry, in
-// 64 x 64 tiles through LDS: 16-byte row pieces in, 16-byte column pieces out.
-// The tiled GEMM reads a column-major B with plain 16-byte LDS reads where a
-// row-major one needs twice as many transposing reads.
+// 128 (k) x 128 (j) tiles through LDS.  Rows come in as 16-byte pieces, eight
+// lanes to a 128-byte row; each thread then reads 16 k-rows x 4 columns as 16
+// dwords, transposes the 4x4 byte blocks in registers (byte permutes) and
+// writes 4 columns x 16 k as 16-byte pieces, eight lanes to a 128-byte column
+// segment, so both sides move whole cache lines.  The dword column of LDS row r
+// is XOR-ed with 4*((r/16)%8), which puts the 64 lanes of a dword read on
+// distinct banks and keeps 16-byte pieces contiguous.  The tiled GEMM reads a
+// column-major B with plain 16-byte LDS reads where a row-major one needs twice
+// as many transposing reads.
+__device__ static inline void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                 uint32_t &o0, uint32_t &o1, uint32_t &o2,
+                                                 uint32_t &o3) {
+    // w_r holds bytes (c0 c1 c2 c3) of row r; o_c receives (r0 r1 r2 r3) of column c
+    const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x05010400u);  // w0b0 w1b0 w0b1 w1b1
+    const uint32_t t1 = __builtin_amdgcn_perm(w3, w2, 0x05010400u);  // w2b0 w3b0 w2b1 w3b1
+    const uint32_t t2 = __builtin_amdgcn_perm(w1, w0, 0x07030602u);  // w0b2 w1b2 w0b3 w1b3
+    const uint32_t t3 = __builtin_amdgcn_perm(w3, w2, 0x07030602u);  // w2b2 w3b2 w2b3 w3b3
+    o0 = __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+    o1 = __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+    o2 = __builtin_amdgcn_perm(t3, t2, 0x05040100u);
+    o3 = __builtin_amdgcn_perm(t3, t2, 0x07060302u);
+}
+
 __global__ __launch_bounds__(256) void transpose_i8(const int8_t *B, int64_t K, int64_t N, int64_t ldb,
                                                     int64_t sB, int8_t *Bt, int64_t ldt, int64_t sBt,
                                                     int tiles_k, int tiles_n, int vec_in) {
-    __shared__ __attribute__((aligned(16))) uint8_t t[64][80];
+    __shared__ __attribute__((aligned(16))) uint32_t t[128 * 32];
     const int tiles = tiles_k * tiles_n;
     const int64_t b = blockIdx.x / tiles;
     const int tile = blockIdx.x - (int)(b * tiles);
-    const int64_t k0 = (int64_t)(tile / tiles_n) * 64, n0 = (int64_t)(tile % tiles_n) * 64;
-    const int r = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 16;
-    const int8_t *src = B + b * sB + (k0 + r) * ldb + n0 + c0;
-    if (vec_in && k0 + r < K && n0 + c0 + 15 < N) {
-        *(intx4 *)&t[r][c0] = *(const intx4 *)src;
-    } else {
+    const int64_t k0 = (int64_t)(tile / tiles_n) * 128, n0 = (int64_t)(tile % tiles_n) * 128;
+    const int tid = threadIdx.x;
+    const int8_t *Bb = B + b * sB;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            t[r][c0 + e] = (k0 + r < K && n0 + c0 + e < N) ? (uint8_t)src[e] : (uint8_t)0;
+    for (int i = 0; i < 4; ++i) {
+        const int f = i * 256 + tid;  // 16-byte piece f: row f/8, bytes 16*(f%8) ..
+        const int r = f >> 3, c = (f & 7) * 16;
+        const int8_t *src = Bb + (k0 + r) * ldb + n0 + c;
+        uint32_t *d = &t[r * 32 + ((c >> 2) ^ (4 * ((r >> 4) & 7)))];
+        if (vec_in && k0 + r < K && n0 + c + 15 < N) {
+            *(intx4 *)d = *(const intx4 *)src;
+        } else {
+            uint8_t *db = (uint8_t *)d;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                db[e] = (k0 + r < K && n0 + c + e < N) ? (uint8_t)src[e] : (uint8_t)0;
+        }
     }
     __syncthreads();
-    const int j = threadIdx.x >> 2, kk = (threadIdx.x & 3) * 16;
-    if (n0 + j >= N) return;
-    int8_t *dst = Bt + b * sBt + (n0 + j) * ldt + k0 + kk;
-    intx4 v;
-    uint8_t *vb = (uint8_t *)&v;
+    // thread: columns 4cg .. 4cg+3, k rows 16kq .. 16kq+15
+    const int kq = tid & 7, cg = tid >> 3;
+    uint32_t w[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) vb[e] = t[kk + e][j];
-    if (k0 + kk + 15 < K) {
-        *(intx4 *)dst = v;
-    } else {
+    for (int e = 0; e < 16; ++e) w[e] = t[(16 * kq + e) * 32 + (cg ^ (4 * kq))];
+    uint32_t o[4][4];  // o[column][group of four k]
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            if (k0 + kk + e < K) dst[e] = (int8_t)vb[e];
+    for (int g = 0; g < 4; ++g)
+        transpose4x4_bytes(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3], o[0][g], o[1][g],
+                           o[2][g], o[3][g]);
+    int8_t *Btb = Bt + b * sBt;
+    const int64_t kb = k0 + 16 * kq;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const int64_t j = n0 + 4 * cg + jj;
+        if (j >= N) continue;
+        int8_t *dst = Btb + j * ldt + kb;
+        const intx4 v = {(int)o[jj][0], (int)o[jj][1], (int)o[jj][2], (int)o[jj][3]};
+        if (kb + 15 < K) {
+            *(intx4 *)dst = v;
+        } else {
+            const uint8_t *vb = (const uint8_t *)&v;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (kb + e < K) dst[e] = (int8_t)vb[e];
+        }
     }
 }
 

@@ -560,7 +560,7 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
     int64_t ldbk = ldb, sBk = sB;
     bool b_colk = b_col;
     if (P.transpose_b) {
-        const int tk = (int)cdiv(K, 64), tn = (int)cdiv(N, 64);
+        const int tk = (int)cdiv(K, 128), tn = (int)cdiv(N, 128);
         const int64_t tgrid = (int64_t)tk * tn * batch;
         if (tgrid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
         const int vec_in = aligned16(B) && ldb % 16 == 0 && sB % 16 == 0;
