@@ -372,6 +372,48 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         // 4-element vector accesses need every row start aligned to 4 elements
         const bool vec_ok = (ldo % 4 == 0) && (CS == 0 || (uintptr_t)Cb % (4 * CS) == 0) &&
                             (uintptr_t)Ob % (4 * DS) == 0;
+        const int64_t row_w = m0 + wm * WTM;
+        if constexpr (TM > 1) {
+            if (vec_ok && row_w + WTM <= p.M && col_w + WTN <= p.N) {
+                // Whole wave tile inside the matrix: the C loads of slab i+1 are
+                // issued before slab i is transposed and stored, so their latency
+                // overlaps that work instead of stalling every slab.
+                vec4 cv[2][PASSES];
+                auto load_c = [&](int i, vec4 (&dst)[PASSES]) {
+#pragma unroll
+                    for (int q = 0; q < PASSES; ++q) {
+                        dst[q] = vec4{0, 0, 0, 0};
+                        if constexpr (CS != 0) {
+                            const int64_t grow = row_w + i * 32 + q * RPP + lane / LPR;
+                            const int64_t gcol = col_w + (lane % LPR) * 4;
+                            dst[q] = load4s<acc_t, CS>(Cb, grow * ldo + gcol, c_f16, true, 4);
+                        }
+                    }
+                };
+                load_c(0, cv[0]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    if (i + 1 < TM) load_c(i + 1, cv[(i + 1) & 1]);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int G = 0; G < 16; ++G)
+                            slab[(8 * (G >> 2) + 4 * (lane >> 5) + (G & 3)) * SP + j * 32 +
+                                 (lane & 31)] = acc[i][j][G];
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+                    for (int q = 0; q < PASSES; ++q) {
+                        const int r = q * RPP + lane / LPR;
+                        const int cl = (lane % LPR) * 4;
+                        const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+                        store4s<acc_t, DS>(Ob, (row_w + i * 32 + r) * ldo + col_w + cl,
+                                           finish4(v, cv[i & 1][q], ep), d_f16, true, 4);
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             // accumulators of rows [i*32, i*32+32) of the wave tile -> LDS, row-major
