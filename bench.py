@@ -29,8 +29,8 @@ sys.path.insert(0, ROOT)
 # int8 8192 OP/clk/CU, fp64 matrix 128 FLOP/clk/CU; HBM3E 8 TB/s.
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.2, "f64": 78.6}
 # the sparse instructions do the dense-equivalent work of a 2:4 A at twice the dense rate
-SPARSE_PEAK_TFLOPS = 5033.2
-SPARSE_CONFIGS = {"SP1"}
+SPARSE_PEAK_TFLOPS = {"f16": 5033.2, "bf16": 5033.2, "i8": 10066.4}
+SPARSE_CONFIGS = {"SP1", "SP2"}
 PEAK_HBM_GBS = 8000.0
 DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # Configs whose bounding roof is HBM rather than the matrix cores (arithmetic
@@ -45,12 +45,17 @@ TRAFFIC_FILES = {"C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md"}
 OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4, "none": 0}
 
 
-def algorithmic_bytes(p, c_type=None, d_type=None) -> int:
-    """Compulsory HBM traffic of one call: A, B and C read once, D written once."""
+def algorithmic_bytes(p, c_type=None, d_type=None, sparse=False) -> int:
+    """Compulsory HBM traffic of one call: A, B and C read once, D written once
+    (a 2:4 A: its kept half plus four index bits per group of four k)."""
     elems = p.C.size
     csz = p.C.itemsize if c_type is None else OUT_SIZE[c_type]
     dsz = p.C.itemsize if d_type is None else OUT_SIZE[d_type]
-    return p.A.nbytes + p.B.nbytes + elems * (csz + dsz)
+    a_bytes = p.A.nbytes
+    if sparse:
+        a_bytes = p.batch * p.M * p.K * (p.A.itemsize // 2 if p.A.itemsize > 1 else 0.5) \
+            + p.batch * p.M * p.K // 8
+    return int(a_bytes + p.B.nbytes + elems * (csz + dsz))
 
 
 def store_c(c_type, C):
@@ -135,7 +140,11 @@ def parity_sample(p, D_host, ex=None, sparse=False):
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     if sparse:
         pruned = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch)
-        Dref, S = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **p.oracle_args())
+        r = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **p.oracle_args())
+        if p.dtype == "i8":
+            ok = bool(np.array_equal(Dg.astype(np.int64), r))
+            return {"checked": n, "exact": ok, "ok": ok}
+        Dref, S = r
         tol = oracle.float_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
         ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
@@ -221,15 +230,17 @@ def main():
     code = DTYPE_CODE[p.dtype]
     label = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch, handle=h)
     if name in SPARSE_CONFIGS:
-        label = f"sparse24 smfmac32x32x32 tile256x256 grid={-(-p.M // 256) * -(-p.N // 256) * p.batch}"
+        ins = "smfmac32x32x64" if p.dtype == "i8" else "smfmac32x32x32"
+        label = f"sparse24 {ins} tile256x256 grid={-(-p.M // 256) * -(-p.N // 256) * p.batch}"
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     args_run = (A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, D.data_ptr(),
                 p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch)
     prune_us = None
     if sparse:
-        kp = dmp.sparse24_kp(p.K)
-        Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int16, device=dev)
+        kp = dmp.sparse24_kp(p.K, code)
+        Ac = torch.empty((p.batch, p.M, kp // 2),
+                         dtype=torch.int8 if p.dtype == "i8" else torch.int16, device=dev)
         meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device=dev)
         # the compression is a one-off preparation of A, timed on its own (after
         # one untimed call that loads the kernel)
@@ -279,9 +290,9 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     D_host = D.cpu().numpy()
 
-    peak = SPARSE_PEAK_TFLOPS if sparse else PEAK_TFLOPS[p.dtype]
+    peak = SPARSE_PEAK_TFLOPS[p.dtype] if sparse else PEAK_TFLOPS[p.dtype]
     unit = "TOP/s" if p.dtype == "i8" else "TFLOP/s"
-    nbytes = algorithmic_bytes(p, *(ex[:2] if ex else (None, None)))
+    nbytes = algorithmic_bytes(p, *(ex[:2] if ex else (None, None)), sparse=sparse)
     if name in HBM_BOUND:
         gbs = nbytes / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -146,9 +146,11 @@ class Handle:
 _default = {}
 
 
-def sparse24_kp(K: int) -> int:
-    """Dense k per compressed row: 64 * ceil(K / 64) (Kp/2 values, Kp/16 index words)."""
-    return -(-K // 64) * 64
+def sparse24_kp(K: int, dtype: int = GEMM_F16) -> int:
+    """Dense k per compressed row (Kp/2 values, Kp/16 16-bit index words):
+    64 * ceil(K / 64) for fp16/bf16, 128 * ceil(K / 128) for int8."""
+    g = 128 if dtype == GEMM_I8 else 64
+    return -(-K // g) * g
 
 
 def default_handle() -> Handle:

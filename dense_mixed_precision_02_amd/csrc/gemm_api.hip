@@ -395,19 +395,22 @@ hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, c
     return launch_tiny_dt<I8>(P.cfg, t, sa, sb, P.grid, s);
 }
 
-// Compressed-A geometry: Kp = 64 * ceil(K / 64) dense k, Kp/2 values and
-// Kp/16 index words per row.
-int64_t sparse_kp(int64_t K) { return cdiv(K, 64) * 64; }
+// Compressed-A geometry: Kp dense k per row (a whole number of the sparse
+// kernel's k-tiles: 64 for fp16/bf16, 128 for int8), Kp/2 values and Kp/16
+// 16-bit index words per row.
+int64_t sparse_kt(int dtype) { return dtype == GEMM_I8 ? 128 : 64; }
+int64_t sparse_kp(int64_t K, int dtype) { return cdiv(K, sparse_kt(dtype)) * sparse_kt(dtype); }
 
 int validate_sparse(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int64_t batch) {
     if (!h) return GEMM_ERR_INVALID_ARG;
-    if (dtype != GEMM_F16 && dtype != GEMM_BF16) return GEMM_ERR_INVALID_ARG;
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16 && dtype != GEMM_I8) return GEMM_ERR_INVALID_ARG;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return GEMM_ERR_INVALID_ARG;
     if (M > (1ll << 31) - 1024 || N > (1ll << 31) - 1024 || K > (1ll << 31) - 1024 ||
         batch > (1ll << 30))
         return GEMM_ERR_INVALID_ARG;
     // byte offsets inside one 256-row panel of the compressed operand fit 31 bits
-    if (256 * (sparse_kp(K) / 2) * 2 >= (1ll << 31) - (1ll << 22)) return GEMM_ERR_INVALID_ARG;
+    if (256 * (sparse_kp(K, dtype) / 2) * elem_size(dtype) >= (1ll << 31) - (1ll << 22))
+        return GEMM_ERR_INVALID_ARG;
     return GEMM_OK;
 }
 
@@ -598,17 +601,21 @@ int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t l
     if (rc != GEMM_OK) return rc;
     if (K > 0 && lda < K) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || batch == 0 || K == 0) return GEMM_OK;
-    if (!A || !Ac || !meta || (uintptr_t)A % 2 || (uintptr_t)Ac % 2 || (uintptr_t)meta % 2)
+    const int esz = elem_size(dtype);
+    if (!A || !Ac || !meta || (uintptr_t)A % esz || (uintptr_t)Ac % esz || (uintptr_t)meta % 2)
         return GEMM_ERR_INVALID_ARG;
-    const int64_t kp = sparse_kp(K);
+    const int64_t kp = sparse_kp(K, dtype);
     const int64_t items = batch * M * (kp / 16);
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(items, 256), 256 * 64));
     hipStream_t s = (hipStream_t)stream;
     if (dtype == GEMM_F16)
         hipLaunchKernelGGL(prune24_kernel<F16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
                            M * lda, batch, Ac, meta, kp / 2, kp / 16);
-    else
+    else if (dtype == GEMM_BF16)
         hipLaunchKernelGGL(prune24_kernel<BF16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
+                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+    else
+        hipLaunchKernelGGL(prune24_kernel<I8>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
                            M * lda, batch, Ac, meta, kp / 2, kp / 16);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -632,16 +639,19 @@ int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const v
                    : GEMM_ERR_HIP;
     // the operands go straight to LDS in 16-byte granules: aligned starts, whole
     // granules along the contiguous extent of B, offsets within 31 bits
-    if (!Ac || !meta || !B || !aligned16(Ac) || !aligned16(meta) || !aligned16(B) || (ldb * 2) % 16 ||
-        (b_col ? K % 8 : N % 8) || (b_col ? 256 * ldb : 64 * ldb) * 2 >= (1ll << 31) - (1ll << 22))
+    const int esz = elem_size(dtype), gran = 16 / esz;
+    const int64_t kt = sparse_kt(dtype);
+    if (!Ac || !meta || !B || !aligned16(Ac) || !aligned16(meta) || !aligned16(B) || ldb % gran ||
+        (b_col ? K % gran : N % gran) ||
+        (b_col ? 256 * ldb : kt * ldb) * esz >= (1ll << 31) - (1ll << 22))
         return GEMM_ERR_INVALID_ARG;
-    const int64_t kp = sparse_kp(K);
+    const int64_t kp = sparse_kp(K, dtype);
     SparseArgs a;
     a.Ac = Ac; a.meta = meta; a.B = B; a.C = C; a.D = D;
     a.M = M; a.N = N; a.K = K; a.ldac = kp / 2; a.ldm = kp / 16; a.ldb = ldb; a.ldc = ldc;
     a.sAc = M * (kp / 2); a.sM = M * (kp / 16); a.sB = (b_col ? N : K) * ldb; a.sC = M * ldc;
     a.tiles_m = (int)cdiv(M, 256); a.tiles_n = (int)cdiv(N, 256); a.batch = (int)batch;
-    a.nkt = (int)(kp / 64);
+    a.nkt = (int)(kp / kt);
     a.ep = ep;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n * batch;
     if (grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
@@ -649,9 +659,12 @@ int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const v
     if (dtype == GEMM_F16) {
         if (b_col) hipLaunchKernelGGL((sparse_gemm<F16, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((sparse_gemm<F16, false>), g, blk, 0, s, a);
-    } else {
+    } else if (dtype == GEMM_BF16) {
         if (b_col) hipLaunchKernelGGL((sparse_gemm<BF16, true>), g, blk, 0, s, a);
         else hipLaunchKernelGGL((sparse_gemm<BF16, false>), g, blk, 0, s, a);
+    } else {
+        if (b_col) hipLaunchKernelGGL((sparse_gemm<I8, true>), g, blk, 0, s, a);
+        else hipLaunchKernelGGL((sparse_gemm<I8, false>), g, blk, 0, s, a);
     }
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }

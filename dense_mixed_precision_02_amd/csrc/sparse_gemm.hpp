@@ -1,21 +1,24 @@
 // sparse_gemm.hpp -- D = A*B + C with a 2:4 structured-sparse A on the sparse
-// matrix instructions v_smfmac_f32_32x32x32_{f16,bf16} (pages: "MFMA common
-// parameters", section "Sparse MFMA parameters": two of every four
-// consecutive K positions of A hold the non-zeros, and an index operand says
-// which).
+// matrix instructions v_smfmac_f32_32x32x32_{f16,bf16} and
+// v_smfmac_i32_32x32x64_i8 (pages: "MFMA common parameters", section "Sparse
+// MFMA parameters": two of every four consecutive K positions of A hold the
+// non-zeros, and an index operand says which, two bits per kept value).
 //
 // Compressed A (the library's format): per row, every group of four dense k
-// keeps two values, the one at the lower position first; a 16-bit index word
-// per 16 dense k (four groups) holds, for value j = 0..7 of those eight, its
-// position inside its group in bits [2j+1:2j].  Rows are padded to Kp dense k,
-// Kp = 64 * ceil(K / 64), with zero values.
+// keeps two values, the one at the lower position first; the index stream
+// holds four bits per group (the two positions, lower one in the low two
+// bits), groups in k order, packed into 16-bit words low nibble first.  Rows
+// are padded to Kp dense k with zero values: Kp = 64 * ceil(K / 64) for
+// fp16/bf16, 128 * ceil(K / 128) for int8 (one k-tile).
 //
-// Instruction maps on gfx950 (checked with a one-hot probe): lane L holds row
-// L%32 of A; its eight compressed values cover dense k [16h, 16h+16) of the
-// 32-k step with h = L/32, and its index word is the one of those 16 k.  B
-// lane L holds column L%32 at dense k 8h..8h+7 and 16+8h..16+8h+7 -- exactly
-// the two 16-k fragments of the dense 32x32x16 instruction for the step's two
-// halves, so B is staged and read exactly as in the dense kernel.
+// Instruction maps on gfx950 (checked with one-hot and random-operand probes):
+// lane L holds row L%32 of A; with h = L/32 its compressed values cover dense k
+// [16h, 16h+16) of the 32-k step (16-bit types: eight values) or [32h, 32h+32)
+// of the 64-k step (int8: sixteen values), and its 32-bit index operand is
+// the index stream of those k, value j's position in bits [2j+1:2j].  B lane L
+// holds column L%32 as the two fragments of the dense 32x32 instruction (16-k
+// or 32-k) for the step's two halves, so B is staged and read exactly as in the
+// dense kernel.
 #pragma once
 
 #include "tile_gemm.hpp"
@@ -34,6 +37,12 @@ template <> struct SparseMma<F16> {
                                                         __builtin_bit_cast(sp_half16, b), c, idx, 0, 0);
     }
 };
+template <> struct SparseMma<I8> {
+    __device__ static intx16 mma(intx4 a, intx4 b0, intx4 b1, intx16 c, int idx) {
+        const sp_intx8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
+    }
+};
 template <> struct SparseMma<BF16> {
     __device__ static floatx16 mma(intx4 a, intx4 b0, intx4 b1, floatx16 c, int idx) {
         const sp_intx8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -47,26 +56,32 @@ struct SparseArgs {
     void *D;
     int64_t M, N, K, ldac, ldm, ldb, ldc;  // ldac = Kp/2 values, ldm = Kp/16 words
     int64_t sAc, sM, sB, sC;               // batch strides in elements
-    int tiles_m, tiles_n, batch, nkt;      // nkt = Kp/64 k-tiles
-    EpiParams ep;                          // plain: fp32 C and D, alpha 1, beta 0 or 1
+    int tiles_m, tiles_n, batch, nkt;      // nkt = Kp/KT k-tiles
+    EpiParams ep;                          // plain: accumulator-typed C and D, alpha 1, beta 0 or 1
 };
 
-// Compressed-A panel: R rows x 32 values (64 dense k) = 64 bytes per row; the
-// 16-byte granule g of row r sits in slot g ^ ((r >> 2) & 3), so that the 16
-// rows one fragment read touches land on distinct banks.
+// Dense k per k-tile: two instruction steps.  Either way a k-tile is 64 bytes
+// of compressed values and 128 bytes of B per row or column; the index stream
+// is KT/8 bytes per row.
+template <class DT> constexpr int sparse_kt() { return DT::ESZ == 2 ? 64 : 128; }
+
+// Compressed-A panel: R rows x 64 bytes (one k-tile) per row; the 16-byte
+// granule g of row r sits in slot g ^ ((r >> 1) & 3), so that any eight
+// consecutive rows of one fragment read cover the eight 16-byte slots of a
+// 128-byte bank window.
 template <int R, int NW>
 struct OpC {
     static constexpr int BYTES = R * 64;
     static constexpr int CHUNKS = BYTES / 1024;  // 16 rows per wave-wide load
     static constexpr int CPW = CHUNKS / NW;
     static_assert(CHUNKS % NW == 0, "chunks split evenly over waves");
-    __device__ static int sw(int r) { return (r >> 2) & 3; }
+    __device__ static int sw(int r) { return (r >> 1) & 3; }
     int off0, r0, step;
-    __device__ void init(int wave, int lane, int64_t ld) {
+    __device__ void init(int wave, int lane, int64_t ld_bytes) {
         r0 = wave * 16 + (lane >> 2);
         const int g = (lane & 3) ^ sw(r0);  // sw(r0 + 16*NW*j) == sw(r0)
-        off0 = (int)(r0 * ld + 8 * g) * 2;
-        step = (int)(16 * NW * ld) * 2;
+        off0 = (int)(r0 * ld_bytes + 16 * g);
+        step = (int)(16 * NW * ld_bytes);
     }
     // chunk j of this wave; rows: valid rows from the tile origin; ok: the k-tile exists
     __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
@@ -74,7 +89,7 @@ struct OpC {
         const bool in = ok && r0 + 16 * NW * j < rows;
         load_granule_to_lds(rs, lds + (j * NW + wave) * 1024, in ? off0 + j * step : OOB_OFFSET);
     }
-    // eight values of row rbase + L%32 for step S (32 dense k): granule 2S + L/32
+    // values of row rbase + L%32 for step S: granule 2S + L/32
     __device__ static intx4 frag(const DMP_LDS char *lds, int rbase, int S, int lane) {
         const int row = rbase + (lane & 31);
         const int g = 2 * S + (lane >> 5);
@@ -82,43 +97,59 @@ struct OpC {
     }
 };
 
-// Index words of a panel: R rows x 4 words (64 dense k) = 8 bytes per row,
-// copied with 4-byte direct loads (two lanes per row).
-template <int R, int NW>
+// Index stream of a panel: R rows x MB bytes (one k-tile) per row, row after
+// row, copied with direct loads of 4 bytes (MB = 8: two lanes per row) or 16
+// bytes (MB = 16), so that each load instruction reads whole row segments.
+// (A dword-major layout would make the index reads free of bank conflicts but
+// needs one row per lane in every load, which costs more than it saves.)
+template <int R, int NW, int MB>
 struct OpMeta {
-    static constexpr int BYTES = R * 8;
-    static constexpr int CHUNKS = BYTES / 256;  // 32 rows per wave-wide load
+    static constexpr int BYTES = R * MB;
+    static constexpr int LB = MB == 8 ? 4 : 16;  // bytes per lane per load
+    static constexpr int LPR = MB / LB;          // lanes per row
+    static constexpr int ROWS = 64 / LPR;        // rows per wave-wide load
+    static constexpr int CHUNKS = R / ROWS;
     static constexpr int CPW = CHUNKS / NW;
+    static_assert(MB == 8 || MB == 16, "index bytes per row");
     static_assert(CHUNKS % NW == 0, "chunks split evenly over waves");
     int off0, r0, step;
-    __device__ void init(int wave, int lane, int64_t ld) {
-        r0 = wave * 32 + (lane >> 1);
-        off0 = (int)(r0 * ld) * 2 + (lane & 1) * 4;
-        step = (int)(32 * NW * ld) * 2;
+    __device__ void init(int wave, int lane, int64_t ld_bytes) {
+        r0 = wave * ROWS + lane / LPR;
+        off0 = (int)(r0 * ld_bytes) + (lane % LPR) * LB;
+        step = (int)(ROWS * NW * ld_bytes);
     }
     __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
                           int64_t rows, bool ok) const {
-        const bool in = ok && r0 + 32 * NW * j < rows;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds + (j * NW + wave) * 256, 4,
-                                                 in ? off0 + j * step : OOB_OFFSET, 0, 0, 0);
+        const bool in = ok && r0 + ROWS * NW * j < rows;
+        DMP_LDS char *dst = lds + (j * NW + wave) * 64 * LB;
+        const int off = in ? off0 + j * step : OOB_OFFSET;
+        if constexpr (LB == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, off, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
     }
+    // index operand of row rbase + L%32 for step S: the 16-bit (MB = 8) or
+    // 32-bit (MB = 16) piece 2S + L/32 of the row's k-tile
     __device__ static int word(const DMP_LDS char *lds, int rbase, int S, int lane) {
         const int row = rbase + (lane & 31);
-        return *(const DMP_LDS uint16_t *)(lds + row * 8 + (2 * S + (lane >> 5)) * 2);
+        if constexpr (MB == 8) return *(const DMP_LDS uint16_t *)(lds + row * 8 + (2 * S + (lane >> 5)) * 2);
+        else return *(const DMP_LDS int *)(lds + row * 16 + (2 * S + (lane >> 5)) * 4);
     }
 };
 
 // 256 x 256 tile of D per workgroup of 4 waves (2 x 2, 128 x 128 each); k-tile
-// of 64 dense k (two instruction steps); three LDS stages so that the copy of
-// k-tile t+2 has two k-tiles of work to land behind.  BKC: B column-major.
+// of two instruction steps; three LDS stages so that the copy of k-tile t+2
+// has two k-tiles of work to land behind.  BKC: B column-major.
 template <class DT, bool BKC>
 __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
     constexpr int BM = 256, BN = 256, NW = 4, WN = 2;
     constexpr int WTM = 128, WTN = 128, TM = WTM / 32, TN = WTN / 32;
-    constexpr int KT = 64;  // dense k per k-tile
+    constexpr int KT = sparse_kt<DT>();  // dense k per k-tile
+    constexpr int ESZ = DT::ESZ;
     using OpA = OpC<BM, NW>;
-    using OpM = OpMeta<BM, NW>;
+    using OpM = OpMeta<BM, NW, KT / 8>;
     using OpB = Operand<DT, BN, NW, BKC>;
+    using acc_t = typename DT::acc;
+    using accv = typename DT::accv;
+    using vec4 = vec4_of<acc_t>;
     constexpr int SP = WTN + 8;  // epilogue slab row (floats)
     constexpr int ABYTES = OpA::BYTES > 32 * SP * 4 ? OpA::BYTES : 32 * SP * 4;
     static_assert(32 * SP * 4 <= OpB::BYTES, "epilogue slab must fit a B buffer");
@@ -149,23 +180,24 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
 
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
-    const char *Acb = (const char *)p.Ac + (int64_t)b * p.sAc * 2;
+    const int64_t ldac_b = p.ldac * ESZ, ldm_b = p.ldm * 2;  // row strides in bytes
+    const char *Acb = (const char *)p.Ac + (int64_t)b * p.sAc * ESZ;
     const char *Mb = (const char *)p.meta + (int64_t)b * p.sM * 2;
-    const char *Bb = (const char *)p.B + (int64_t)b * p.sB * 2;
+    const char *Bb = (const char *)p.B + (int64_t)b * p.sB * ESZ;
     const int64_t rows_a = p.M - m0;
 
     OpA opa;
     OpM opm;
     OpB opb;
-    opa.init(wave, lane, p.ldac);
-    opm.init(wave, lane, p.ldm);
+    opa.init(wave, lane, ldac_b);
+    opm.init(wave, lane, ldm_b);
     opb.init(wave, lane, p.ldb, (int)n0, p.N);
 
-    floatx16 acc[TM][TN];
+    accv acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = floatx16{};
+        for (int j = 0; j < TN; ++j) acc[i][j] = accv{};
 
     // The k-tile count is made a multiple of three (one per LDS stage, named
     // statically) by leading all-zero k-tiles; tiles outside [0, nkt) load zeros
@@ -178,8 +210,8 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
         const int64_t ktc = ok ? kt : 0;
         const int64_t kl = p.K - ktc * KT;
         const int kleft = !ok ? 0 : (kl > KT ? KT : (kl < 0 ? 0 : (int)kl));
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Acb + (m0 * p.ldac + ktc * (KT / 2)) * 2);
-        const __amdgpu_buffer_rsrc_t rm = make_rsrc(Mb + (m0 * p.ldm + ktc * (KT / 16)) * 2);
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Acb + m0 * ldac_b + ktc * 64);
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(Mb + m0 * ldm_b + ktc * (KT / 8));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(OpB::tile_base(Bb, p.ldb, n0, ktc * KT));
 #pragma unroll
         for (int j = 0; j < OpA::CPW; ++j) opa.issue(ra, la, wave, j, rows_a, ok);
@@ -254,11 +286,11 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
     // slab per wave, C and D as 16-byte vectors), fp32 C and D ----
     wait_vmcnt<0>();
     __syncthreads();
-    DMP_LDS float *slab = (DMP_LDS float *)(wave == 0 ? LB[0] : wave == 1 ? LB[1] : wave == 2 ? LB[2] : LA[0]);
+    DMP_LDS acc_t *slab = (DMP_LDS acc_t *)(wave == 0 ? LB[0] : wave == 1 ? LB[1] : wave == 2 ? LB[2] : LA[0]);
     constexpr int LPR = WTN / 4, RPP = 64 / LPR, PASSES = 32 / RPP;
     const int64_t col_w = n0 + wn * WTN;
-    const float *Cb = (const float *)p.C + (int64_t)b * p.sC;
-    float *Db = (float *)p.D + (int64_t)b * p.sC;
+    const acc_t *Cb = (const acc_t *)p.C + (int64_t)b * p.sC;
+    acc_t *Db = (acc_t *)p.D + (int64_t)b * p.sC;
     const bool use_c = p.ep.use_c;
     const bool vec_ok = p.ldc % 4 == 0 && (!use_c || (uintptr_t)Cb % 16 == 0) && (uintptr_t)Db % 16 == 0;
 #pragma unroll
@@ -271,20 +303,20 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const int64_t row_s = m0 + wm * WTM + i * 32;
         if (vec_ok && row_s + 32 <= p.M && col_w + WTN <= p.N) {
-            floatx4 cv[PASSES];
+            vec4 cv[PASSES];
 #pragma unroll
             for (int q = 0; q < PASSES; ++q) {
-                cv[q] = floatx4{0, 0, 0, 0};
+                cv[q] = vec4{0, 0, 0, 0};
                 if (use_c) {
                     const int64_t grow = row_s + q * RPP + lane / LPR, gcol = col_w + (lane % LPR) * 4;
-                    cv[q] = *(const floatx4 *)(Cb + grow * p.ldc + gcol);
+                    cv[q] = *(const vec4 *)(Cb + grow * p.ldc + gcol);
                 }
             }
 #pragma unroll
             for (int q = 0; q < PASSES; ++q) {
                 const int r = q * RPP + lane / LPR, cl = (lane % LPR) * 4;
-                const floatx4 v = *(const DMP_LDS floatx4 *)(slab + r * SP + cl);
-                *(floatx4 *)(Db + (row_s + r) * p.ldc + col_w + cl) = finish4(v, cv[q], p.ep);
+                const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+                *(vec4 *)(Db + (row_s + r) * p.ldc + col_w + cl) = finish4(v, cv[q], p.ep);
             }
         } else {
 #pragma unroll 1
@@ -292,10 +324,10 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
                 const int r = q * RPP + lane / LPR, cl = (lane % LPR) * 4;
                 const int64_t grow = row_s + r, gcol = col_w + cl;
                 const int nn = grow < p.M ? cols_in(p.N, gcol) : 0;
-                const floatx4 c = use_c ? load4s<float, 4>(Cb, grow * p.ldc + gcol, false, vec_ok, nn)
-                                        : floatx4{0, 0, 0, 0};
-                const floatx4 v = *(const DMP_LDS floatx4 *)(slab + r * SP + cl);
-                store4s<float, 4>(Db, grow * p.ldc + gcol, finish4(v, c, p.ep), false, vec_ok, nn);
+                const vec4 c = use_c ? load4s<acc_t, 4>(Cb, grow * p.ldc + gcol, false, vec_ok, nn)
+                                     : vec4{0, 0, 0, 0};
+                const vec4 v = *(const DMP_LDS vec4 *)(slab + r * SP + cl);
+                store4s<acc_t, 4>(Db, grow * p.ldc + gcol, finish4(v, c, p.ep), false, vec_ok, nn);
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -305,7 +337,7 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
 // Compression: one thread per (batch entry, row, 16 dense k).  Keeps in every
 // group of four k the two entries of largest magnitude (ties to the lower k;
 // positions past K never win over present ones) and writes the eight kept
-// values and their index word.  A is row-major.
+// values and their 16-bit piece of the index stream.  A is row-major.
 template <class DT>
 __global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, int64_t K,
                                                       int64_t lda, int64_t sA, int64_t batch,
@@ -316,19 +348,21 @@ __global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, 
          x += (int64_t)gridDim.x * blockDim.x) {
         const int64_t c = x % quads, ri = x / quads;
         const int64_t i = ri % M, b = ri / M;
-        const uint16_t *row = (const uint16_t *)A + b * sA + i * lda;
-        uint16_t v[16];
+        using E = typename DT::elem;
+        const E *row = (const E *)A + b * sA + i * lda;
+        E v[16];
         float mag[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int64_t k = c * 16 + e;
-            v[e] = k < K ? row[k] : (uint16_t)0;
-            const float f = DT::ESZ == 2 && std::is_same<DT, F16>::value
-                                ? (float)__builtin_bit_cast(_Float16, v[e])
-                                : __builtin_bit_cast(float, (uint32_t)v[e] << 16);
+            v[e] = k < K ? row[k] : (E)0;
+            float f;  // exact value of the entry
+            if constexpr (std::is_same<DT, F16>::value) f = (float)__builtin_bit_cast(_Float16, (uint16_t)v[e]);
+            else if constexpr (std::is_same<DT, BF16>::value) f = __builtin_bit_cast(float, (uint32_t)(uint16_t)v[e] << 16);
+            else f = (float)v[e];
             mag[e] = k < K ? __builtin_fabsf(f) : -1.0f;
         }
-        uint16_t outv[8];
+        E outv[8];
         uint32_t word = 0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -348,7 +382,7 @@ __global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, 
             outv[2 * u + 1] = v[4 * u + keep[1]];
             word |= (uint32_t)(keep[0] | (keep[1] << 2)) << (4 * u);
         }
-        uint16_t *dst = (uint16_t *)Ac + b * M * ldac + i * ldac + c * 8;
+        E *dst = (E *)Ac + b * M * ldac + i * ldac + c * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e] = outv[e];
         ((uint16_t *)meta)[b * M * ldm + i * ldm + c] = (uint16_t)word;

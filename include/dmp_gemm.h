@@ -147,33 +147,37 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
  * parameters", section "Sparse MFMA parameters": two of every four consecutive
  * K positions of A hold the non-zeros, and an index operand names them).
  *
- * gemm_prune24 compresses a row-major A (fp16 or bf16, M x K, lda >= K, batch
- * entries M*lda elements apart): in every group of four consecutive k of a row
- * (the last group of a row may be shorter) the two entries of largest magnitude
- * are kept -- on a tie the lower k; positions past K never win over present
- * ones; inputs are taken to be finite -- and the others dropped.  Output, with
- * Kp = 64 * ceil(K / 64):
+ * gemm_prune24 compresses a row-major A (fp16, bf16 or int8, M x K, lda >= K,
+ * batch entries M*lda elements apart): in every group of four consecutive k of
+ * a row (the last group of a row may be shorter) the two entries of largest
+ * magnitude are kept -- on a tie the lower k; positions past K never win over
+ * present ones; float inputs are taken to be finite -- and the others dropped.
+ * Output, with Kp = 64 * ceil(K / 64) for fp16/bf16 and 128 * ceil(K / 128)
+ * for int8:
  *   Ac:   batch x M x Kp/2 values of A's type, row-major; for group q of row i
  *         Ac[i][2q] is the kept value at the lower position, Ac[i][2q+1] the other;
  *         groups past K hold zeros;
  *   meta: batch x M x Kp/16 uint16; word w of row i covers groups 4w..4w+3, and
  *         its bits [2j+1:2j] are the position (0..3) inside its group of value
- *         j = 0..7 of Ac[i][8w .. 8w+8).
- * Pointers need 2-byte alignment here; gemm_run_sparse24 needs Ac and meta
- * 16-byte aligned (hipMalloc'd buffers are).
+ *         j = 0..7 of Ac[i][8w .. 8w+8) (the same bits for every input type:
+ *         four per group, groups in k order, low bits first).
+ * Pointers need element alignment (meta: 2 bytes) here; gemm_run_sparse24
+ * needs Ac and meta 16-byte aligned (hipMalloc'd buffers are).
  */
 int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t lda, int dtype,
                  int64_t batch, void *Ac, void *meta, void *stream);
 
 /*
  * D_b = prune(A_b) * B_b + C_b from the compressed form written by
- * gemm_prune24 (same M, K, dtype and batch), on v_smfmac_f32_32x32x32.  B is
- * K x N fp16/bf16 like A, row-major (default) or GEMM_B_COLMAJOR (the only flag
- * taken), batch entries (K or N)*ldb elements apart; C and D fp32, row-major,
- * ldc >= N, batch entries M*ldc apart; D may alias C exactly.  Accuracy as
- * gemm_run's fp16/bf16 bound with the pruned A.  Requirements (else
- * GEMM_ERR_INVALID_ARG, nothing enqueued): B 16-byte aligned, ldb a multiple of
- * 8 elements, and N (row-major B) or K (column-major B) a multiple of 8.
+ * gemm_prune24 (same M, K, dtype and batch), on v_smfmac_f32_32x32x32_{f16,bf16}
+ * or v_smfmac_i32_32x32x64_i8.  B is K x N of A's type, row-major (default) or
+ * GEMM_B_COLMAJOR (the only flag taken), batch entries (K or N)*ldb elements
+ * apart; C and D fp32 (fp16/bf16) or int32 (int8), row-major, ldc >= N, batch
+ * entries M*ldc apart; D may alias C exactly.  Accuracy as gemm_run's with the
+ * pruned A: the fp16/bf16 bound, int8 exact (int32, wrapping).  Requirements
+ * (else GEMM_ERR_INVALID_ARG, nothing enqueued): B 16-byte aligned, ldb a
+ * multiple of 16 bytes, and N (row-major B) or K (column-major B) a multiple
+ * of 16 bytes' worth of elements (8 for fp16/bf16, 16 for int8).
  * K == 0 gives D = C.
  */
 int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const void *B,

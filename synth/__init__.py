@@ -158,6 +158,10 @@ CONFIGS = {
     # problems, A/B row-major uniform[-1,1], C fp32 uniform[-1,1]
     "T1": dict(dtype="f16", M=4, N=4, K=16, batch=1 << 20, seed=8, ab_dist="uniform",
                ab_range=(-1.0, 1.0), c_dist="uniform", c_range=(-1.0, 1.0)),
+    # 2:4 structured-sparse int8 A: C3's 8192^3 distributions, B column-major (the
+    # layout the sparse kernel reads without transposing), seed 10
+    "SP2": dict(dtype="i8", M=8192, N=8192, K=8192, b_col=True, seed=10, ab_dist="uniform_int",
+                c_dist="uniform_int", c_range=(-(1 << 20), 1 << 20)),
 }
 
 CONFIG_LABELS = {
@@ -170,6 +174,7 @@ CONFIG_LABELS = {
     "F1": "gemm 4096x4096x4096 fp64 (row-major), C fp64",
     "T1": "batched gemm 1048576 x 4x4x16 fp16 (row-major), C fp32",
     "SP1": "gemm 4096x4096x4096 bf16, A 2:4-pruned (row-major), B col-major, C fp32 zeros",
+    "SP2": "gemm 8192x8192x8192 int8, A 2:4-pruned (row-major), B col-major, C int32, bit-exact",
 }
 
 

@@ -23,19 +23,29 @@ def handle():
     h.close()
 
 
-def kp_of(K):
-    return -(-K // 64) * 64
+def kp_of(K, dtype="f16"):
+    g = 128 if dtype == "i8" else 64
+    return -(-K // g) * g
 
 
 def dev16(x):
-    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+    """Operand storage on the device (16-bit patterns as int16, int8 as is)."""
+    x = np.ascontiguousarray(x)
+    return torch.from_numpy(x if x.dtype == np.int8 else x.view(np.int16)).cuda()
+
+
+def host_bits(t, dtype):
+    """Device operand storage back as the oracle's storage type."""
+    x = t.cpu().numpy()
+    return x if dtype == "i8" else x.view(np.uint16)
 
 
 def compress(handle, p, Ad=None):
     """gemm_prune24 on p's A; returns device (Ac, meta)."""
-    kp = kp_of(p.K)
+    kp = kp_of(p.K, p.dtype)
     Ad = dev16(p.A) if Ad is None else Ad
-    Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int16, device="cuda")
+    Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int8 if p.dtype == "i8" else torch.int16,
+                     device="cuda")
     meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device="cuda")
     rc = handle.prune24(Ad.data_ptr(), p.M, p.K, p.lda, DTYPE_CODE[p.dtype], p.batch,
                         Ac.data_ptr(), meta.data_ptr(), torch.cuda.current_stream().cuda_stream)
@@ -46,10 +56,10 @@ def compress(handle, p, Ad=None):
 def expected_compressed(p):
     """Ac and index words built from the oracle's kept positions."""
     pruned, keep = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch, return_keep=True)
-    kp = kp_of(p.K)
+    kp = kp_of(p.K, p.dtype)
     keep_p = np.zeros((p.batch, p.M, kp), dtype=bool)
     keep_p[:, :, :p.K] = keep
-    vals = np.zeros((p.batch, p.M, kp), dtype=np.uint16)
+    vals = np.zeros((p.batch, p.M, kp), dtype=p.A.dtype)
     vals[:, :, :p.K] = p.A[:, :p.M, :p.K]
     # groups with fewer than two present positions keep the lowest absent ones
     g = keep_p.reshape(p.batch, p.M, kp // 4, 4)
@@ -59,7 +69,7 @@ def expected_compressed(p):
     pos = np.argsort(~g, axis=-1, kind="stable")[..., :2]          # kept positions, ascending
     v4 = vals.reshape(p.batch, p.M, kp // 4, 4)
     Ac = np.take_along_axis(v4, pos, axis=-1).reshape(p.batch, p.M, kp // 2)
-    Ac = np.where(np.take_along_axis(g, pos, -1).reshape(Ac.shape), Ac, 0).astype(np.uint16)
+    Ac = np.where(np.take_along_axis(g, pos, -1).reshape(Ac.shape), Ac, 0).astype(p.A.dtype)
     bits = (pos[..., 0] | (pos[..., 1] << 2)).astype(np.uint32)    # 4 bits per group
     w = bits.reshape(p.batch, p.M, kp // 16, 4)
     meta = (w[..., 0] | (w[..., 1] << 4) | (w[..., 2] << 8) | (w[..., 3] << 12)).astype(np.uint16)
@@ -81,6 +91,16 @@ def run_sparse(handle, p, Ac, meta, C=None, D=None):
 def check(p, pruned, Dg, exact=False, pts=None):
     args = p.oracle_args()
     Dg = Dg.reshape(p.batch, p.M, p.ldc)[:, :, :p.N]
+    if p.dtype == "i8":   # int32 results: bit for bit
+        if pts is not None:
+            ref = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **args)
+            got = Dg[pts[:, 0], pts[:, 1], pts[:, 2]].astype(np.int64)
+        else:
+            ref = oracle.gemm(p.dtype, pruned, p.B, p.C, **args)
+            got = Dg.astype(np.int64)
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{len(bad)} int32 results differ, first at {bad[0]}"
+        return 0.0
     if pts is not None:
         ref, S = oracle.gemm_points(p.dtype, pruned, p.B, p.C, pts, **args)
         got = Dg[pts[:, 0], pts[:, 1], pts[:, 2]].astype(np.float64)
@@ -103,34 +123,74 @@ def test_workload_4096_cubed(handle):
     log(f"[sparse] {synth.CONFIG_LABELS['SP1']}")
     Ac, meta = compress(handle, p)
     pruned, eAc, emeta = expected_compressed(p)
-    assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc), "compressed values differ"
+    assert np.array_equal(host_bits(Ac, p.dtype), eAc), "compressed values differ"
     assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta), "index words differ"
     Dg = run_sparse(handle, p, Ac, meta)
     r = check(p, pruned, Dg, pts=sample_points(p, 3000, seed=91))
     log(f"[sparse] ok, max err/bound {r:.3g}")
 
 
+def test_workload_int8_8192_cubed(handle):
+    p = synth.config_problem("SP2")
+    log(f"[sparse] {synth.CONFIG_LABELS['SP2']}")
+    Ac, meta = compress(handle, p)
+    # compressor against the oracle's pruning on a block of rows (the whole
+    # expected form at this size would hold ~1 GB of host temporaries)
+    rows = 512
+    q = synth.Problem("i8", rows, p.N, p.K, 1, p.lda, p.ldb, p.ldc, False, True,
+                      np.ascontiguousarray(p.A[:, 4096:4096 + rows]), p.B[:, :1],
+                      p.C[:, :rows], name="SP2 rows 4096..4607")
+    _, eAc, emeta = expected_compressed(q)
+    assert np.array_equal(host_bits(Ac, "i8")[:, 4096:4096 + rows], eAc), "compressed values differ"
+    assert np.array_equal(meta.cpu().numpy().view(np.uint16)[:, 4096:4096 + rows], emeta)
+    del eAc, emeta
+    C = torch.from_numpy(p.C).cuda()
+    D = torch.empty_like(C)
+    Dg = run_sparse(handle, p, Ac, meta, C=C, D=D)
+    pruned = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch)
+    check(p, pruned, Dg, pts=sample_points(p, 3000, seed=96))
+    log("[sparse] int8 ok (sampled, bit-exact)")
+
+
+def test_int8_ties_and_extremes(handle):
+    """Equal magnitudes of opposite sign (-v and v tie; the lower k wins), -128
+    (magnitude 128, above every other value), zeros, K not a multiple of four."""
+    rng = np.random.default_rng(97)
+    p = synth.make_problem("i8", 200, 48, 203, c_range=(-(1 << 20), 1 << 20), seed=98)
+    p.A = rng.choice(np.array([-128, -3, 3, 0, 127, -127, 1, -1], dtype=np.int8),
+                     size=p.A.shape).astype(np.int8)
+    Ac, meta = compress(handle, p)
+    pruned, eAc, emeta = expected_compressed(p)
+    assert np.array_equal(host_bits(Ac, p.dtype), eAc)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+    check(p, pruned, run_sparse(handle, p, Ac, meta))
+
+
 SHAPES = [(256, 256, 64), (300, 264, 200), (1, 8, 1000), (520, 136, 64 * 5), (256, 512, 4096 + 64),
-          (77, 40, 24)]
+          (77, 40, 24), (264, 272, 128 * 3 + 16)]
 
 
-@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("b_col", [False, True])
 def test_shapes_layouts(handle, dtype, b_col):
+    gran = 16 if dtype == "i8" else 8   # elements per 16-byte granule
     for n, (M, N, K) in enumerate(SHAPES):
-        if b_col and K % 8:
+        if (K if b_col else N) % gran:
             continue
+        ckw = dict(c_range=(-(1 << 20), 1 << 20)) if dtype == "i8" else {}
         for batch in (1, 3):
-            p = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=400 + n)
+            p = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=400 + n, **ckw)
             log(f"[sparse] {dtype} {batch} x {M}x{N}x{K} b_col={b_col}")
             Ac, meta = compress(handle, p)
             pruned, eAc, emeta = expected_compressed(p)
-            assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc)
+            assert np.array_equal(host_bits(Ac, p.dtype), eAc)
             assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
             check(p, pruned, run_sparse(handle, p, Ac, meta))
             # exact-integer inputs: every partial sum an integer, so bit for bit
             e = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=500 + n,
-                                   ab_dist="small_int", c_dist="small_int", c_range=(-8, 8))
+                                   ab_dist="small_int",
+                                   c_dist="uniform_int" if dtype == "i8" else "small_int",
+                                   c_range=(-8, 8))
             Ac, meta = compress(handle, e)
             pruned, _, _ = expected_compressed(e)
             check(e, pruned, run_sparse(handle, e, Ac, meta), exact=True)
@@ -146,7 +206,7 @@ def test_ties_padding_and_lda(handle):
     p.A = synth.f64_to_f16_bits(rng.choice([-1.0, 0.0, 1.0, 0.5, -0.5], size=(1, p.M, p.lda)))
     Ac, meta = compress(handle, p)
     pruned, eAc, emeta = expected_compressed(p)
-    assert np.array_equal(Ac.cpu().numpy().view(np.uint16), eAc)
+    assert np.array_equal(host_bits(Ac, p.dtype), eAc)
     assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
     check(p, pruned, run_sparse(handle, p, Ac, meta))
 
@@ -167,8 +227,9 @@ def test_k_zero_alias_and_invalid(handle):
     check(q, pruned, run_sparse(handle, q, Ac, meta, C=C, D=C))   # D aliases C
     B = dev16(q.B)
     D = torch.full_like(C, 3.0)
-    bad = [dict(dtype=2), dict(dtype=0, flags=1), dict(flags=4), dict(Bp=B.data_ptr() + 2),
-           dict(N=100), dict(ldb=260), dict(ldc=100), dict(Acp=Ac.data_ptr() + 2)]
+    bad = [dict(dtype=3), dict(dtype=5), dict(dtype=0, flags=1), dict(flags=4), dict(Bp=B.data_ptr() + 2),
+           dict(N=100), dict(ldb=260), dict(ldc=100), dict(Acp=Ac.data_ptr() + 2),
+           dict(dtype=2, N=248), dict(dtype=2, ldb=264)]   # int8: whole 16-element granules
     for kw in bad:
         a = dict(Acp=Ac.data_ptr(), Mp=meta.data_ptr(), Bp=B.data_ptr(), N=256, ldb=256, ldc=256,
                  dtype=1, flags=0)

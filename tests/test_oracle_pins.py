@@ -580,3 +580,32 @@ def test_prune24_brute_force_and_properties():
             assert np.array_equal(P[b, :, p.K:], p.A[b, :, p.K:])
         # idempotent, and a 2:4 matrix is its own pruning
         assert np.array_equal(oracle.prune24(dtype, P, M=p.M, K=p.K, lda=p.lda, batch=2), P)
+
+
+def test_prune24_int8_hand_example_and_brute_force():
+    """int8: magnitude is |v| of the integer (-128 has the largest, 128), ties
+    keep the lower k; brute force over every candidate pair on random tie-heavy
+    rows."""
+    A = np.array([[[-128, 127, 0, -127, 3, -3, 3, 1, 0, 0, 0, -1, 5, -5, 2]]], dtype=np.int8)
+    P = oracle.prune24("i8", A, M=1, K=15, lda=15)
+    # {-128,127,0,-127}: -128 and 127; {3,-3,3,1}: first two (|3| ties, lower k);
+    # {0,0,0,-1}: -1 and the first 0; short group {5,-5,2}: 5 and -5
+    want = np.array([[[-128, 127, 0, 0, 3, -3, 0, 0, 0, 0, 0, -1, 5, -5, 0]]], dtype=np.int8)
+    assert np.array_equal(P, want)
+    rng = np.random.default_rng(14)
+    A = rng.choice(np.array([-128, -2, -1, 0, 1, 2, 127], dtype=np.int8), size=(2, 7, 41))
+    P = oracle.prune24("i8", A, M=7, K=38, lda=41, batch=2)
+    v = A.astype(np.int64)
+    for b in range(2):
+        for i in range(7):
+            for g in range(0, 38, 4):
+                ks = list(range(g, min(g + 4, 38)))
+
+                def beats(x, y):
+                    return abs(v[b, i, x]) > abs(v[b, i, y]) or (abs(v[b, i, x]) == abs(v[b, i, y]) and x < y)
+                cands = [set(x) for x in itertools.combinations(ks, min(2, len(ks)))
+                         if all(beats(u, w) for u in x for w in ks if w not in x)]
+                assert len(cands) == 1
+                for k in ks:
+                    assert P[b, i, k] == (A[b, i, k] if k in cands[0] else 0)
+        assert np.array_equal(P[b, :, 38:], A[b, :, 38:])
