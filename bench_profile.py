@@ -5,6 +5,8 @@
     python bench_profile.py traffic --gemm-fetch A.csv --gemm-write B.csv \
         --copy-fetch C.csv --copy-write D.csv --copy-bytes N --kernel tile_gemm \
         --cmd "<commands>" --out profiles/Y.md
+    python bench_profile.py counters A.csv [B.csv ...] --kernel NAME --cmd "<commands>" \
+        --out profiles/Z.md [--us MICROSECONDS]
 
 The traffic summary scales the per-dispatch FETCH_SIZE / WRITE_SIZE of the GEMM
 kernel by the ratio (known bytes / counter bytes) that the same counters show
@@ -104,6 +106,58 @@ def cmd_traffic(a):
     sys.stdout.write(text)
 
 
+def cmd_counters(a):
+    """Per-dispatch medians of every counter in one or more --pmc CSVs for one
+    kernel, plus the ratios they support (MI355X: 8 XCDs x 16 L2 channels,
+    256 CUs, 1024 SIMDs; GRBM_GUI_ACTIVE summed over the XCDs)."""
+    med = {}
+    durs = []
+    for path in a.csv:
+        names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
+        for n in names:
+            v = per_dispatch(path, n, a.kernel)
+            if v:
+                med[n] = statistics.median(v[2:] or v)
+        seen = {}
+        for r in csv.DictReader(open(path)):
+            if a.kernel in r["Kernel_Name"] and "Start_Timestamp" in r:
+                seen[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        durs += [seen[k] for k in sorted(seen, key=int)][2:]
+    us = a.us if a.us else (statistics.median(durs) if durs else None)
+    lines = ["# rocprofv3 counters of one kernel launch (median over dispatches)", "",
+             f"commands: {a.cmd}", f"kernel: {a.kernel}",
+             f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    for n in sorted(med):
+        lines.append(f"{n}: {med[n]:.6g}")
+    g = med.get("GRBM_GUI_ACTIVE")
+    if g:
+        cyc = g / 8.0
+        lines += ["", f"cycles per XCD (GRBM_GUI_ACTIVE / 8): {cyc:.0f}"]
+        if us:
+            lines.append(f"launch duration (median, counter runs): {us:.1f} us; "
+                         f"effective clock {cyc / us / 1e3:.2f} GHz")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            lines.append(f"MFMA busy (per SIMD): {100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cyc:.1f} %")
+        if "TCC_BUSY_avr" in med:
+            lines.append(f"L2 channel busy (TCC_BUSY_avr / cycles): {100 * med['TCC_BUSY_avr'] / cyc:.1f} %")
+        if "TA_BUSY_avr" in med:
+            lines.append(f"address unit busy (TA_BUSY_avr / cycles): {100 * med['TA_BUSY_avr'] / cyc:.1f} %")
+        if "TCP_PENDING_STALL_CYCLES_sum" in med:
+            lines.append(f"L1 stalled on pending L2 data: "
+                         f"{100 * med['TCP_PENDING_STALL_CYCLES_sum'] / 256 / cyc:.1f} % of cycles per CU")
+    if "TCC_HIT_sum" in med and "TCC_MISS_sum" in med:
+        h, m = med["TCC_HIT_sum"], med["TCC_MISS_sum"]
+        lines.append(f"L2 hit rate: {100 * h / (h + m):.1f} %")
+    if "TCP_TCC_READ_REQ_sum" in med:
+        r = med["TCP_TCC_READ_REQ_sum"]
+        lines.append(f"L1->L2 read requests: {r:.4g} (64 or 128 B each)")
+        if "TCP_TCC_READ_REQ_LATENCY_sum" in med:
+            lines.append(f"mean L2 read latency seen by L1: {med['TCP_TCC_READ_REQ_LATENCY_sum'] / r:.0f} cycles")
+    text = "\n".join(lines) + "\n"
+    open(a.out, "w").write(text)
+    sys.stdout.write(text)
+
+
 def read_traffic(path: str):
     """(bytes per launch, source hash) from a traffic summary, or None."""
     if not os.path.exists(path):
@@ -132,8 +186,14 @@ def main():
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--kernel", default="tile_gemm")
     t.add_argument("--copy-kernel", default="copyBuffer")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--us", type=float, default=None, help="launch duration, for the clock")
     a = ap.parse_args()
-    (cmd_stats if a.what == "stats" else cmd_traffic)(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
