@@ -238,10 +238,10 @@ def main():
                 p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch)
     prune_us = None
     if sparse:
-        kp = dmp.sparse24_kp(p.K, code)
-        Ac = torch.empty((p.batch, p.M, kp // 2),
+        kp, mp = dmp.sparse24_kp(p.K, code), dmp.sparse24_mp(p.M)
+        Ac = torch.empty((p.batch, mp, kp // 2),
                          dtype=torch.int8 if p.dtype == "i8" else torch.int16, device=dev)
-        meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device=dev)
+        meta = torch.empty((p.batch, mp, kp // 16), dtype=torch.int16, device=dev)
         # the compression is a one-off preparation of A, timed on its own (after
         # one untimed call that loads the kernel)
         rc = h.prune24(A.data_ptr(), p.M, p.K, p.lda, code, p.batch, Ac.data_ptr(), meta.data_ptr(),

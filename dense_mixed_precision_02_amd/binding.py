@@ -153,6 +153,11 @@ def sparse24_kp(K: int, dtype: int = GEMM_F16) -> int:
     return -(-K // g) * g
 
 
+def sparse24_mp(M: int) -> int:
+    """Rows of the compressed form: 16 * ceil(M / 16) (16-row blocks)."""
+    return -(-M // 16) * 16
+
+
 def default_handle() -> Handle:
     import torch
     dev = torch.cuda.current_device()

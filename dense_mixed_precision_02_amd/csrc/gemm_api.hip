@@ -397,9 +397,10 @@ hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, c
 
 // Compressed-A geometry: Kp dense k per row (a whole number of the sparse
 // kernel's k-tiles: 64 for fp16/bf16, 128 for int8), Kp/2 values and Kp/16
-// 16-bit index words per row.
+// 16-bit index words per row, Mp = 16 * ceil(M / 16) rows (16-row blocks).
 int64_t sparse_kt(int dtype) { return dtype == GEMM_I8 ? 128 : 64; }
 int64_t sparse_kp(int64_t K, int dtype) { return cdiv(K, sparse_kt(dtype)) * sparse_kt(dtype); }
+int64_t sparse_mp(int64_t M) { return cdiv(M, 16) * 16; }
 
 int validate_sparse(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int dtype, int64_t batch) {
     if (!h) return GEMM_ERR_INVALID_ARG;
@@ -604,19 +605,19 @@ int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t l
     const int esz = elem_size(dtype);
     if (!A || !Ac || !meta || (uintptr_t)A % esz || (uintptr_t)Ac % esz || (uintptr_t)meta % 2)
         return GEMM_ERR_INVALID_ARG;
-    const int64_t kp = sparse_kp(K, dtype);
-    const int64_t items = batch * M * (kp / 16);
+    const int64_t kp = sparse_kp(K, dtype), mp = sparse_mp(M), nkt = kp / sparse_kt(dtype);
+    const int64_t items = batch * mp * (kp / 16);
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(cdiv(items, 256), 256 * 64));
     hipStream_t s = (hipStream_t)stream;
     if (dtype == GEMM_F16)
-        hipLaunchKernelGGL(prune24_kernel<F16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
-                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+        hipLaunchKernelGGL(prune24_kernel<F16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, mp, K,
+                           lda, M * lda, batch, Ac, meta, nkt);
     else if (dtype == GEMM_BF16)
-        hipLaunchKernelGGL(prune24_kernel<BF16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
-                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+        hipLaunchKernelGGL(prune24_kernel<BF16>, dim3((unsigned)grid), dim3(256), 0, s, A, M, mp, K,
+                           lda, M * lda, batch, Ac, meta, nkt);
     else
-        hipLaunchKernelGGL(prune24_kernel<I8>, dim3((unsigned)grid), dim3(256), 0, s, A, M, K, lda,
-                           M * lda, batch, Ac, meta, kp / 2, kp / 16);
+        hipLaunchKernelGGL(prune24_kernel<I8>, dim3((unsigned)grid), dim3(256), 0, s, A, M, mp, K,
+                           lda, M * lda, batch, Ac, meta, nkt);
     return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
@@ -645,11 +646,11 @@ int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const v
         (b_col ? K % gran : N % gran) ||
         (b_col ? 256 * ldb : kt * ldb) * esz >= (1ll << 31) - (1ll << 22))
         return GEMM_ERR_INVALID_ARG;
-    const int64_t kp = sparse_kp(K, dtype);
+    const int64_t kp = sparse_kp(K, dtype), mp = sparse_mp(M);
     SparseArgs a;
     a.Ac = Ac; a.meta = meta; a.B = B; a.C = C; a.D = D;
-    a.M = M; a.N = N; a.K = K; a.ldac = kp / 2; a.ldm = kp / 16; a.ldb = ldb; a.ldc = ldc;
-    a.sAc = M * (kp / 2); a.sM = M * (kp / 16); a.sB = (b_col ? N : K) * ldb; a.sC = M * ldc;
+    a.M = M; a.N = N; a.K = K; a.ldb = ldb; a.ldc = ldc;
+    a.sAc = mp * (kp / 2); a.sM = mp * (kp / 16); a.sB = (b_col ? N : K) * ldb; a.sC = M * ldc;
     a.tiles_m = (int)cdiv(M, 256); a.tiles_n = (int)cdiv(N, 256); a.batch = (int)batch;
     a.nkt = (int)(kp / kt);
     a.ep = ep;

@@ -9,7 +9,11 @@
 // holds four bits per group (the two positions, lower one in the low two
 // bits), groups in k order, packed into 16-bit words low nibble first.  Rows
 // are padded to Kp dense k with zero values: Kp = 64 * ceil(K / 64) for
-// fp16/bf16, 128 * ceil(K / 128) for int8 (one k-tile).
+// fp16/bf16, 128 * ceil(K / 128) for int8 (one sparse k-tile of KT dense k),
+// and to Mp = 16 * ceil(M / 16) rows.  Both arrays are blocked so that one
+// k-tile of 16 rows is contiguous: values [batch][Mp/16][Kp/KT][16][KT/2]
+// (1 KB per block and k-tile), index words [batch][Mp/16][Kp/KT][16][KT/16];
+// each copy then reads whole 128-byte lines.
 //
 // Instruction maps on gfx950 (checked with one-hot and random-operand probes):
 // lane L holds row L%32 of A; with h = L/32 its compressed values cover dense k
@@ -54,8 +58,8 @@ template <> struct SparseMma<BF16> {
 struct SparseArgs {
     const void *Ac, *meta, *B, *C;
     void *D;
-    int64_t M, N, K, ldac, ldm, ldb, ldc;  // ldac = Kp/2 values, ldm = Kp/16 words
-    int64_t sAc, sM, sB, sC;               // batch strides in elements
+    int64_t M, N, K, ldb, ldc;
+    int64_t sAc, sM, sB, sC;               // batch strides in elements (values, words, B, C)
     int tiles_m, tiles_n, batch, nkt;      // nkt = Kp/KT k-tiles
     EpiParams ep;                          // plain: accumulator-typed C and D, alpha 1, beta 0 or 1
 };
@@ -68,7 +72,8 @@ template <class DT> constexpr int sparse_kt() { return DT::ESZ == 2 ? 64 : 128; 
 // Compressed-A panel: R rows x 64 bytes (one k-tile) per row; the 16-byte
 // granule g of row r sits in slot g ^ ((r >> 1) & 3), so that any eight
 // consecutive rows of one fragment read cover the eight 16-byte slots of a
-// 128-byte bank window.
+// 128-byte bank window.  One wave-wide load copies one 16-row block (1 KB,
+// contiguous in the blocked format); blk is the distance between blocks.
 template <int R, int NW>
 struct OpC {
     static constexpr int BYTES = R * 64;
@@ -77,11 +82,11 @@ struct OpC {
     static_assert(CHUNKS % NW == 0, "chunks split evenly over waves");
     __device__ static int sw(int r) { return (r >> 1) & 3; }
     int off0, r0, step;
-    __device__ void init(int wave, int lane, int64_t ld_bytes) {
+    __device__ void init(int wave, int lane, int64_t blk) {
         r0 = wave * 16 + (lane >> 2);
         const int g = (lane & 3) ^ sw(r0);  // sw(r0 + 16*NW*j) == sw(r0)
-        off0 = (int)(r0 * ld_bytes + 16 * g);
-        step = (int)(16 * NW * ld_bytes);
+        off0 = (int)(wave * blk) + (lane >> 2) * 64 + 16 * g;
+        step = (int)(NW * blk);
     }
     // chunk j of this wave; rows: valid rows from the tile origin; ok: the k-tile exists
     __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
@@ -98,25 +103,27 @@ struct OpC {
 };
 
 // Index stream of a panel: R rows x MB bytes (one k-tile) per row, row after
-// row, copied with direct loads of 4 bytes (MB = 8: two lanes per row) or 16
-// bytes (MB = 16), so that each load instruction reads whole row segments.
-// (A dword-major layout would make the index reads free of bank conflicts but
-// needs one row per lane in every load, which costs more than it saves.)
+// row in LDS, copied with direct loads of 4 bytes (MB = 8: two lanes per row)
+// or 16 bytes (MB = 16).  In the blocked format a 16-row block's index bytes
+// for one k-tile are contiguous (16*MB bytes, blocks blk apart), so each
+// load reads whole lines.
 template <int R, int NW, int MB>
 struct OpMeta {
     static constexpr int BYTES = R * MB;
     static constexpr int LB = MB == 8 ? 4 : 16;  // bytes per lane per load
     static constexpr int LPR = MB / LB;          // lanes per row
     static constexpr int ROWS = 64 / LPR;        // rows per wave-wide load
+    static constexpr int BPC = ROWS / 16;        // 16-row blocks per load
     static constexpr int CHUNKS = R / ROWS;
     static constexpr int CPW = CHUNKS / NW;
     static_assert(MB == 8 || MB == 16, "index bytes per row");
     static_assert(CHUNKS % NW == 0, "chunks split evenly over waves");
     int off0, r0, step;
-    __device__ void init(int wave, int lane, int64_t ld_bytes) {
+    __device__ void init(int wave, int lane, int64_t blk) {
         r0 = wave * ROWS + lane / LPR;
-        off0 = (int)(r0 * ld_bytes) + (lane % LPR) * LB;
-        step = (int)(ROWS * NW * ld_bytes);
+        const int lpb = 64 / BPC;                 // lanes per block
+        off0 = (int)((BPC * wave + lane / lpb) * blk) + (lane % lpb) * LB;
+        step = (int)(BPC * NW * blk);
     }
     __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
                           int64_t rows, bool ok) const {
@@ -180,17 +187,18 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
 
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / WN, wn = wave % WN;
-    const int64_t ldac_b = p.ldac * ESZ, ldm_b = p.ldm * 2;  // row strides in bytes
-    const char *Acb = (const char *)p.Ac + (int64_t)b * p.sAc * ESZ;
-    const char *Mb = (const char *)p.meta + (int64_t)b * p.sM * 2;
+    // blocked format: 16-row blocks, each k-tile of a block contiguous
+    const int64_t vblk = (int64_t)p.nkt * 1024, mblk = (int64_t)p.nkt * 16 * (KT / 8);
+    const char *Acb = (const char *)p.Ac + (int64_t)b * p.sAc * ESZ + (m0 / 16) * vblk;
+    const char *Mb = (const char *)p.meta + (int64_t)b * p.sM * 2 + (m0 / 16) * mblk;
     const char *Bb = (const char *)p.B + (int64_t)b * p.sB * ESZ;
     const int64_t rows_a = p.M - m0;
 
     OpA opa;
     OpM opm;
     OpB opb;
-    opa.init(wave, lane, ldac_b);
-    opm.init(wave, lane, ldm_b);
+    opa.init(wave, lane, vblk);
+    opm.init(wave, lane, mblk);
     opb.init(wave, lane, p.ldb, (int)n0, p.N);
 
     accv acc[TM][TN];
@@ -210,8 +218,8 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
         const int64_t ktc = ok ? kt : 0;
         const int64_t kl = p.K - ktc * KT;
         const int kleft = !ok ? 0 : (kl > KT ? KT : (kl < 0 ? 0 : (int)kl));
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Acb + m0 * ldac_b + ktc * 64);
-        const __amdgpu_buffer_rsrc_t rm = make_rsrc(Mb + m0 * ldm_b + ktc * (KT / 8));
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(Acb + ktc * 1024);
+        const __amdgpu_buffer_rsrc_t rm = make_rsrc(Mb + ktc * 16 * (KT / 8));
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(OpB::tile_base(Bb, p.ldb, n0, ktc * KT));
 #pragma unroll
         for (int j = 0; j < OpA::CPW; ++j) opa.issue(ra, la, wave, j, rows_a, ok);
@@ -334,33 +342,37 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
     }
 }
 
-// Compression: one thread per (batch entry, row, 16 dense k).  Keeps in every
-// group of four k the two entries of largest magnitude (ties to the lower k;
-// positions past K never win over present ones) and writes the eight kept
-// values and their 16-bit piece of the index stream.  A is row-major.
+// Compression: one thread per (batch entry, row, 16 dense k), rows up to Mp.
+// Keeps in every group of four k the two entries of largest magnitude (ties to
+// the lower k; positions past K, and every position of a padding row, never
+// win over present ones) and writes the eight kept values and their 16-bit
+// piece of the index stream into the blocked format.  A is row-major.
 template <class DT>
-__global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, int64_t K,
+__global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, int64_t Mp, int64_t K,
                                                       int64_t lda, int64_t sA, int64_t batch,
-                                                      void *Ac, void *meta, int64_t ldac, int64_t ldm) {
-    const int64_t quads = ldm;  // Kp / 16
-    const int64_t total = batch * M * quads;
+                                                      void *Ac, void *meta, int64_t nkt) {
+    constexpr int KT = sparse_kt<DT>();
+    const int64_t quads = nkt * (KT / 16);  // 16-k pieces per row
+    const int64_t total = batch * Mp * quads;
     for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < total;
          x += (int64_t)gridDim.x * blockDim.x) {
         const int64_t c = x % quads, ri = x / quads;
-        const int64_t i = ri % M, b = ri / M;
+        const int64_t i = ri % Mp, b = ri / Mp;
+        const bool row_in = i < M;
         using E = typename DT::elem;
-        const E *row = (const E *)A + b * sA + i * lda;
+        const E *row = (const E *)A + b * sA + (row_in ? i : 0) * lda;
         E v[16];
         float mag[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int64_t k = c * 16 + e;
-            v[e] = k < K ? row[k] : (E)0;
+            const bool in = row_in && k < K;
+            v[e] = in ? row[k] : (E)0;
             float f;  // exact value of the entry
             if constexpr (std::is_same<DT, F16>::value) f = (float)__builtin_bit_cast(_Float16, (uint16_t)v[e]);
             else if constexpr (std::is_same<DT, BF16>::value) f = __builtin_bit_cast(float, (uint32_t)(uint16_t)v[e] << 16);
             else f = (float)v[e];
-            mag[e] = k < K ? __builtin_fabsf(f) : -1.0f;
+            mag[e] = in ? __builtin_fabsf(f) : -1.0f;
         }
         E outv[8];
         uint32_t word = 0;
@@ -382,10 +394,13 @@ __global__ __launch_bounds__(256) void prune24_kernel(const void *A, int64_t M, 
             outv[2 * u + 1] = v[4 * u + keep[1]];
             word |= (uint32_t)(keep[0] | (keep[1] << 2)) << (4 * u);
         }
-        E *dst = (E *)Ac + b * M * ldac + i * ldac + c * 8;
+        // block (b, i/16), k-tile t, row i%16, piece q of the k-tile
+        const int64_t t = c / (KT / 16), q = c % (KT / 16);
+        const int64_t blk = (b * (Mp / 16) + i / 16) * nkt + t;
+        E *dst = (E *)Ac + blk * 16 * (KT / 2) + (i % 16) * (KT / 2) + q * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) dst[e] = outv[e];
-        ((uint16_t *)meta)[b * M * ldm + i * ldm + c] = (uint16_t)word;
+        ((uint16_t *)meta)[blk * 16 * (KT / 16) + (i % 16) * (KT / 16) + q] = (uint16_t)word;
     }
 }
 

@@ -152,15 +152,22 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
  * a row (the last group of a row may be shorter) the two entries of largest
  * magnitude are kept -- on a tie the lower k; positions past K never win over
  * present ones; float inputs are taken to be finite -- and the others dropped.
- * Output, with Kp = 64 * ceil(K / 64) for fp16/bf16 and 128 * ceil(K / 128)
- * for int8:
- *   Ac:   batch x M x Kp/2 values of A's type, row-major; for group q of row i
- *         Ac[i][2q] is the kept value at the lower position, Ac[i][2q+1] the other;
- *         groups past K hold zeros;
- *   meta: batch x M x Kp/16 uint16; word w of row i covers groups 4w..4w+3, and
- *         its bits [2j+1:2j] are the position (0..3) inside its group of value
- *         j = 0..7 of Ac[i][8w .. 8w+8) (the same bits for every input type:
- *         four per group, groups in k order, low bits first).
+ * Output, with KT = 64 (fp16/bf16) or 128 (int8) dense k per sparse k-tile,
+ * Kp = KT * ceil(K / KT), T = Kp / KT and Mp = 16 * ceil(M / 16):
+ *   row data: for row i, value slot 2q of its Kp/2 slots holds the kept value
+ *         of group q (k 4q..4q+3) at the lower position, slot 2q+1 the other;
+ *         index word w (of Kp/16) covers groups 4w..4w+3 and its bits
+ *         [2j+1:2j] are the position (0..3) inside its group of value slot
+ *         8w + j (the same bits for every input type: four per group, groups
+ *         in k order, low bits first).  Groups past K and rows M..Mp-1 hold
+ *         zero values (their index words name positions 0 and 1).
+ *   Ac:   batch x Mp x Kp/2 values of A's type, blocked: value slot s of row
+ *         i lies at element ((b*(Mp/16) + i/16)*T + s/(KT/2))*16*(KT/2)
+ *         + (i%16)*(KT/2) + s%(KT/2) -- one k-tile of 16 rows is 1 KB,
+ *         contiguous, so that the product's copies read whole cache lines;
+ *   meta: batch x Mp x Kp/16 uint16, blocked the same way: word w of row i at
+ *         ((b*(Mp/16) + i/16)*T + w/(KT/16))*16*(KT/16) + (i%16)*(KT/16)
+ *         + w%(KT/16).
  * Pointers need element alignment (meta: 2 bytes) here; gemm_run_sparse24
  * needs Ac and meta 16-byte aligned (hipMalloc'd buffers are).
  */

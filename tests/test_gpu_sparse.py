@@ -23,9 +23,48 @@ def handle():
     h.close()
 
 
+def kt_of(dtype):
+    """Dense k per sparse k-tile."""
+    return 128 if dtype == "i8" else 64
+
+
 def kp_of(K, dtype="f16"):
-    g = 128 if dtype == "i8" else 64
+    g = kt_of(dtype)
     return -(-K // g) * g
+
+
+def mp_of(M):
+    return -(-M // 16) * 16
+
+
+def blocked(x, per_kt, fill):
+    """Row-major compressed rows (batch, M, n) -> the library's blocked layout
+    (batch, Mp/16, n/per_kt, 16, per_kt); padding rows hold `fill`."""
+    b, M, n = x.shape
+    Mp = mp_of(M)
+    y = np.full((b, Mp, n), fill, dtype=x.dtype)
+    y[:, :M] = x
+    return y.reshape(b, Mp // 16, 16, n // per_kt, per_kt).transpose(0, 1, 3, 2, 4)
+
+
+def gpu_blocked(t, dtype, per_kt, cols):
+    """Device compressed array -> (batch, Mp/16, cols/per_kt, 16, per_kt)."""
+    x = t.cpu().numpy()
+    if x.dtype != np.int8:
+        x = x.view(np.uint16)
+    b, Mp = x.shape[0], x.shape[1]
+    return x.reshape(b, Mp // 16, cols // per_kt, 16, per_kt)
+
+
+def same_compressed(p, Ac, meta, eAc, emeta, blocks=slice(None)):
+    """GPU (Ac, meta) equal to the expected row-major forms (rows of `blocks` only)."""
+    kt = kt_of(p.dtype)
+    kp = kp_of(p.K, p.dtype)
+    ga = gpu_blocked(Ac, p.dtype, kt // 2, kp // 2)[:, blocks]
+    gm = gpu_blocked(meta, p.dtype, kt // 16, kp // 16)[:, blocks]
+    # rows past M: zero values, index words naming positions 0 and 1
+    return (np.array_equal(ga, blocked(eAc, kt // 2, 0)) and
+            np.array_equal(gm, blocked(emeta, kt // 16, 0x4444)))
 
 
 def dev16(x):
@@ -34,19 +73,13 @@ def dev16(x):
     return torch.from_numpy(x if x.dtype == np.int8 else x.view(np.int16)).cuda()
 
 
-def host_bits(t, dtype):
-    """Device operand storage back as the oracle's storage type."""
-    x = t.cpu().numpy()
-    return x if dtype == "i8" else x.view(np.uint16)
-
-
 def compress(handle, p, Ad=None):
     """gemm_prune24 on p's A; returns device (Ac, meta)."""
-    kp = kp_of(p.K, p.dtype)
+    kp, mp = kp_of(p.K, p.dtype), mp_of(p.M)
     Ad = dev16(p.A) if Ad is None else Ad
-    Ac = torch.empty((p.batch, p.M, kp // 2), dtype=torch.int8 if p.dtype == "i8" else torch.int16,
+    Ac = torch.empty((p.batch, mp, kp // 2), dtype=torch.int8 if p.dtype == "i8" else torch.int16,
                      device="cuda")
-    meta = torch.empty((p.batch, p.M, kp // 16), dtype=torch.int16, device="cuda")
+    meta = torch.empty((p.batch, mp, kp // 16), dtype=torch.int16, device="cuda")
     rc = handle.prune24(Ad.data_ptr(), p.M, p.K, p.lda, DTYPE_CODE[p.dtype], p.batch,
                         Ac.data_ptr(), meta.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert rc == 0
@@ -54,7 +87,7 @@ def compress(handle, p, Ad=None):
 
 
 def expected_compressed(p):
-    """Ac and index words built from the oracle's kept positions."""
+    """Ac and index words (row-major, M rows) built from the oracle's kept positions."""
     pruned, keep = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch, return_keep=True)
     kp = kp_of(p.K, p.dtype)
     keep_p = np.zeros((p.batch, p.M, kp), dtype=bool)
@@ -123,8 +156,7 @@ def test_workload_4096_cubed(handle):
     log(f"[sparse] {synth.CONFIG_LABELS['SP1']}")
     Ac, meta = compress(handle, p)
     pruned, eAc, emeta = expected_compressed(p)
-    assert np.array_equal(host_bits(Ac, p.dtype), eAc), "compressed values differ"
-    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta), "index words differ"
+    assert same_compressed(p, Ac, meta, eAc, emeta), "compressed values or index words differ"
     Dg = run_sparse(handle, p, Ac, meta)
     r = check(p, pruned, Dg, pts=sample_points(p, 3000, seed=91))
     log(f"[sparse] ok, max err/bound {r:.3g}")
@@ -141,8 +173,7 @@ def test_workload_int8_8192_cubed(handle):
                       np.ascontiguousarray(p.A[:, 4096:4096 + rows]), p.B[:, :1],
                       p.C[:, :rows], name="SP2 rows 4096..4607")
     _, eAc, emeta = expected_compressed(q)
-    assert np.array_equal(host_bits(Ac, "i8")[:, 4096:4096 + rows], eAc), "compressed values differ"
-    assert np.array_equal(meta.cpu().numpy().view(np.uint16)[:, 4096:4096 + rows], emeta)
+    assert same_compressed(p, Ac, meta, eAc, emeta, blocks=slice(4096 // 16, (4096 + rows) // 16))
     del eAc, emeta
     C = torch.from_numpy(p.C).cuda()
     D = torch.empty_like(C)
@@ -161,8 +192,7 @@ def test_int8_ties_and_extremes(handle):
                      size=p.A.shape).astype(np.int8)
     Ac, meta = compress(handle, p)
     pruned, eAc, emeta = expected_compressed(p)
-    assert np.array_equal(host_bits(Ac, p.dtype), eAc)
-    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+    assert same_compressed(p, Ac, meta, eAc, emeta)
     check(p, pruned, run_sparse(handle, p, Ac, meta))
 
 
@@ -183,8 +213,7 @@ def test_shapes_layouts(handle, dtype, b_col):
             log(f"[sparse] {dtype} {batch} x {M}x{N}x{K} b_col={b_col}")
             Ac, meta = compress(handle, p)
             pruned, eAc, emeta = expected_compressed(p)
-            assert np.array_equal(host_bits(Ac, p.dtype), eAc)
-            assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+            assert same_compressed(p, Ac, meta, eAc, emeta)
             check(p, pruned, run_sparse(handle, p, Ac, meta))
             # exact-integer inputs: every partial sum an integer, so bit for bit
             e = synth.make_problem(dtype, M, N, K, batch=batch, b_col=b_col, seed=500 + n,
@@ -206,8 +235,7 @@ def test_ties_padding_and_lda(handle):
     p.A = synth.f64_to_f16_bits(rng.choice([-1.0, 0.0, 1.0, 0.5, -0.5], size=(1, p.M, p.lda)))
     Ac, meta = compress(handle, p)
     pruned, eAc, emeta = expected_compressed(p)
-    assert np.array_equal(host_bits(Ac, p.dtype), eAc)
-    assert np.array_equal(meta.cpu().numpy().view(np.uint16), emeta)
+    assert same_compressed(p, Ac, meta, eAc, emeta)
     check(p, pruned, run_sparse(handle, p, Ac, meta))
 
 
