@@ -102,9 +102,10 @@ __global__ __launch_bounds__(256) void splitk_reduce(const T *__restrict__ W, co
         vec acc = {0, 0, 0, 0};
         if (S > 0) {
             if constexpr (VEC) {
-                acc = *(const vec *)(W + e);
+                // each partial is read once: non-temporal
+                acc = __builtin_nontemporal_load((const vec *)(W + e));
                 for (int q = 1; q < S; ++q) {
-                    const vec w = *(const vec *)(W + (int64_t)q * total + e);
+                    const vec w = __builtin_nontemporal_load((const vec *)(W + (int64_t)q * total + e));
 #pragma unroll
                     for (int t = 0; t < 4; ++t) acc[t] = add_acc(acc[t], w[t]);
                 }
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void transpose_i8(const int8_t *B, int64_t K, 
         const int8_t *src = Bb + (k0 + r) * ldb + n0 + c;
         uint32_t *d = &t[r * 32 + ((c >> 2) ^ (4 * ((r >> 4) & 7)))];
         if (vec_in && k0 + r < K && n0 + c + 15 < N) {
-            *(intx4 *)d = *(const intx4 *)src;
+            *(intx4 *)d = __builtin_nontemporal_load((const intx4 *)src);  // B is read once
         } else {
             uint8_t *db = (uint8_t *)d;
 #pragma unroll

@@ -82,10 +82,13 @@ __device__ static inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base) {
 }
 
 // 16-byte global -> LDS copy that bypasses registers.  The LDS destination of
-// lane L is lds + 16*L (lds must be wave-uniform).
+// lane L is lds + 16*L (lds must be wave-uniform).  CPOL: cache policy bits of
+// the load (CPOL_NT: non-temporal, for data that no other workgroup reads).
+constexpr int CPOL_NT = 2;
+template <int CPOL = 0>
 __device__ static inline void load_granule_to_lds(__amdgpu_buffer_rsrc_t r, DMP_LDS void *lds,
                                                   int voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voffset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voffset, 0, 0, CPOL);
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding

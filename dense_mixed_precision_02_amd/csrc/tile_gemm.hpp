@@ -106,13 +106,14 @@ struct Operand {
     // Issue chunk j of this wave's share of the copy of one k-tile into LDS
     // buffer `lds`.  rs: buffer over element (row0, k0) of the operand.
     // kleft: valid k elements from k0.
+    template <int CPOL = 0>
     __device__ void issue(const __amdgpu_buffer_rsrc_t &rs, DMP_LDS char *lds, int wave, int j,
                           int kleft, int64_t Rtot) const {
         const int c = j * NW + wave;
         bool ok;
         if (KCONTIG) ok = (row_or_k + 8 * NW * j < Rtot) && (fixed < kleft);
         else ok = (fixed < Rtot) && (row_or_k + KSTEP * j < kleft);
-        load_granule_to_lds(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
+        load_granule_to_lds<CPOL>(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
     }
 
     // LDS reads one fragment takes
@@ -245,6 +246,10 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     // part still has two steps to land before the next barrier.
     constexpr int NCH = OpA::CPW + OpB::CPW;
     constexpr int P1 = (NCH + 1) / 2, P2 = NCH;
+    // 64x64 tiles serve batches of small problems, whose operands no other
+    // workgroup reads: their copies are non-temporal.  Larger tiles share
+    // panels through L2 and keep the default policy.
+    constexpr int CPOL = (BM == 64 && BN == 64) ? CPOL_NT : 0;
     auto stage_part = [&](int kt, DMP_LDS char *la, DMP_LDS char *lb, auto lo_c, auto hi_c) {
         constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
         // k-tiles outside [k_begin, k_end) (the padding tile, and the ones past
@@ -258,8 +263,8 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(OpB::tile_base(Bb, p.ldb, n0, k0));
 #pragma unroll
         for (int c = LO; c < HI; ++c) {
-            if (c < OpA::CPW) opa.issue(ra, la, wave, c, kleft, p.M);
-            else opb.issue(rb, lb, wave, c - OpA::CPW, kleft, p.N);
+            if (c < OpA::CPW) opa.template issue<CPOL>(ra, la, wave, c, kleft, p.M);
+            else opb.template issue<CPOL>(rb, lb, wave, c - OpA::CPW, kleft, p.N);
         }
     };
     using Z = std::integral_constant<int, 0>;

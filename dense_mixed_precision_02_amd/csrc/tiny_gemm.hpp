@@ -134,7 +134,8 @@ struct Stager {
 #pragma unroll
         for (int u = 0; u < PIECES; ++u) {
             const int64_t c = lane + 64 * u;
-            if (c < full) v[u] = *(const intx4 *)(src + c * 16);
+            // non-temporal: each problem's operands are read by this wave only
+            if (c < full) v[u] = __builtin_nontemporal_load((const intx4 *)(src + c * 16));
         }
     }
     __device__ void put(DMP_LDS char *dst, const char *src, int64_t nbytes, int lane) const {
