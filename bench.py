@@ -36,6 +36,12 @@ DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # Configs whose bounding roof is HBM rather than the matrix cores (arithmetic
 # intensity below the ~315 FLOP/byte ridge).
 HBM_BOUND = {"C4", "T1"}
+# Configs whose HBM traffic matters: the timed steps rotate over ROTATE_SETS
+# device copies of the operands and outputs, so that a step never finds the
+# previous step's data in the 256 MB memory-side cache (each config's
+# footprint is above 256 MB, two sets above 512 MB).
+ROTATE = {"C4", "C5", "T1"}
+ROTATE_SETS = 2
 METRIC = "GEMM TFLOPS/TOPS (fp16, bf16, int8) on 1 MI355X; % of dense MFMA peak"
 COPY_BYTES = 512 << 20
 # rocprofv3 HBM-traffic summary of the dominant kernel of each workload
@@ -176,6 +182,9 @@ def main():
     ap.add_argument("--c-type", choices=["f32", "f16", "bf16", "none"], default="f32")
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--beta", type=float, default=1.0)
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="device copies of the inputs and outputs the timed steps rotate over "
+                         f"(default {ROTATE_SETS} for {sorted(ROTATE)}, else 1)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (counter calibration)")
     args = ap.parse_args()
@@ -234,8 +243,14 @@ def main():
         label = f"sparse24 {ins} tile256x256 grid={-(-p.M // 256) * -(-p.N // 256) * p.batch}"
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    args_run = (A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, D.data_ptr(),
-                p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch)
+    nsets = args.rotate if args.rotate else (ROTATE_SETS if name in ROTATE else 1)
+    if sparse:
+        nsets = 1  # the sparse products time one compressed A
+    # set 0 is (A, B, C, D); further sets are device copies of the same inputs
+    sets = [(A, B, C, D)] + [(A.clone(), B.clone(), None if C is None else C.clone(),
+                              torch.empty_like(D)) for _ in range(nsets - 1)]
+    runs = [(a.data_ptr(), b.data_ptr(), c.data_ptr() if c is not None else 0, d.data_ptr(),
+             p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch) for (a, b, c, d) in sets]
     prune_us = None
     if sparse:
         kp, mp = dmp.sparse24_kp(p.K, code), dmp.sparse24_mp(p.M)
@@ -257,31 +272,31 @@ def main():
         assert rc == 0, rc
         prune_us = q0.elapsed_time(q1) * 1e3
 
-        def step():
+        def step(i):
             rc2 = h.run_sparse24(Ac.data_ptr(), meta.data_ptr(), B.data_ptr(), C.data_ptr(),
                                  D.data_ptr(), p.M, p.N, p.K, p.ldb, p.ldc, code, flags, p.batch, sp)
             assert rc2 == 0, rc2
     elif ex is None:
-        def step():
-            h.run(*args_run, sp)
+        def step(i):
+            h.run(*runs[i % nsets], sp)
     else:
         OUTC = {"f32": dmp.GEMM_OUT_F32, "f16": dmp.GEMM_OUT_F16, "bf16": dmp.GEMM_OUT_BF16,
                 "none": dmp.GEMM_OUT_F32}
         kw = dict(alpha=ex[2], beta=ex[3], c_type=OUTC[ex[0]], d_type=OUTC[ex[1]], stream=sp)
 
-        def step():
-            h.run_ex(*args_run, **kw)
+        def step(i):
+            h.run_ex(*runs[i % nsets], **kw)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     # events on the stream the kernels are launched on
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -323,7 +338,7 @@ def main():
                    "b_layout": "col" if p.b_col else "row", "plan": label,
                    "pct_of_dense_peak": round(100 * tflops / peak, 2),
                    "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                   "timed_wall_s": round(wall, 3)},
+                   "timed_wall_s": round(wall, 3), "input_sets": nsets},
         "roofline": roof,
         "parity": parity_sample(p, D_host, ex, sparse),
     }
