@@ -169,7 +169,7 @@ def parity_sample(p, D_host, ex=None, sparse=False):
     return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
@@ -187,7 +187,7 @@ def main():
                          f"(default {ROTATE_SETS} for {sorted(ROTATE)}, else 1)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (counter calibration)")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
