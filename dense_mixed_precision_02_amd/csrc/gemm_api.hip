@@ -20,7 +20,7 @@ using namespace dmp;
 struct gemm_handle {
     int device = 0;
     int num_cus = 0;
-    void *ws = nullptr;   // split-K partials, grown on demand
+    void *ws = nullptr;   // split-K partials or the transposed int8 B, grown on demand
     size_t ws_bytes = 0;
 };
 
@@ -66,6 +66,16 @@ EpiParams plain_epi(int dtype) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Largest element index (plus one) of `batch` contiguous blocks of `rows` rows
+// `ld` apart (`cols` used per row), computed in 128 bits.  Every operand is
+// required to stay within 2^48 elements, far above any device's memory, so
+// that all index arithmetic on the host and in the kernels fits 64 bits.
+bool extent_ok(int64_t batch, int64_t rows, int64_t ld, int64_t cols) {
+    const __int128 stride = (__int128)rows * ld;
+    const __int128 e = (__int128)(batch - 1) * stride + (__int128)(rows - 1) * ld + cols;
+    return e <= ((__int128)1 << 48);
+}
+
 int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const void *D,
              int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
              unsigned flags, int64_t batch, bool check_ptrs, const EpiParams &ep) {
@@ -98,6 +108,12 @@ int validate(gemm_handle_t h, const void *A, const void *B, const void *C, const
         batch > (1ll << 30))
         return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    const bool a_sh = flags & GEMM_A_SHARED, b_sh = flags & GEMM_B_SHARED;
+    const int64_t ar = a_col ? K : M, ac = a_col ? M : K, br = b_col ? N : K, bc = b_col ? K : N;
+    if (K > 0 && (!extent_ok(a_sh ? 1 : batch, ar, lda, ac) ||
+                  !extent_ok(b_sh ? 1 : batch, br, ldb, bc)))
+        return GEMM_ERR_INVALID_ARG;
+    if (!extent_ok(batch, M, ldc, N)) return GEMM_ERR_INVALID_ARG;
     if (!check_ptrs) return GEMM_OK;
     if (!D || (ep.use_c && !C)) return GEMM_ERR_INVALID_ARG;
     if (K > 0 && (!A || !B)) return GEMM_ERR_INVALID_ARG;
@@ -502,7 +518,9 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
     hipStream_t s = (hipStream_t)stream;
     const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
     const bool a_sh = flags & GEMM_A_SHARED, b_sh = flags & GEMM_B_SHARED;
-    const int64_t sA = a_sh ? 0 : (a_col ? K : M) * lda, sB = b_sh ? 0 : (b_col ? N : K) * ldb;
+    // (A and B are not read when K == 0, and their leading dimensions unchecked)
+    const int64_t sA = (a_sh || K == 0) ? 0 : (a_col ? K : M) * lda;
+    const int64_t sB = (b_sh || K == 0) ? 0 : (b_col ? N : K) * ldb;
     const int64_t sC = M * ldc;
     const Plan P = make_plan(h, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
     if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
@@ -602,6 +620,9 @@ int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t l
     if (rc != GEMM_OK) return rc;
     if (K > 0 && lda < K) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || batch == 0 || K == 0) return GEMM_OK;
+    if (!extent_ok(batch, M, lda, K) ||
+        !extent_ok(batch, sparse_mp(M), sparse_kp(K, dtype) / 2, sparse_kp(K, dtype) / 2))
+        return GEMM_ERR_INVALID_ARG;
     const int esz = elem_size(dtype);
     if (!A || !Ac || !meta || (uintptr_t)A % esz || (uintptr_t)Ac % esz || (uintptr_t)meta % 2)
         return GEMM_ERR_INVALID_ARG;
@@ -631,6 +652,10 @@ int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const v
     if (K > 0 && ldb < std::max<int64_t>(1, b_col ? K : N)) return GEMM_ERR_INVALID_ARG;
     if (ldc < std::max<int64_t>(1, N)) return GEMM_ERR_INVALID_ARG;
     if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    if (!extent_ok(batch, M, ldc, N)) return GEMM_ERR_INVALID_ARG;
+    if (K > 0 && (!extent_ok(batch, b_col ? N : K, ldb, b_col ? K : N) ||
+                  !extent_ok(batch, sparse_mp(M), sparse_kp(K, dtype) / 2, sparse_kp(K, dtype) / 2)))
+        return GEMM_ERR_INVALID_ARG;
     if (!C || !D || (uintptr_t)C % 4 || (uintptr_t)D % 4) return GEMM_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     const EpiParams ep = plain_epi(dtype);

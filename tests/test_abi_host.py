@@ -66,10 +66,26 @@ def plan_status(*args):
     (4, 4, 8, 8, 4, 4, -1, 0, 1),          # bad dtype
     (4, 4, 8, 8, 4, 4, 0, 16, 1),          # unknown flag bit
     (4, 4, 8, 8, 4, 4, 0, 0, -1),          # negative batch
+    (4, 4, 8, 1 << 62, 4, 4, 0, 0, 1),     # lda beyond 2^48 elements
+    (4, 4, 8, 8, 1 << 50, 4, 0, 0, 1),     # ldb beyond 2^48 elements
+    (4, 4, 8, 8, 4, 1 << 62, 0, 0, 1),     # ldc beyond 2^48 elements
+    (1 << 20, 1 << 20, 8, 8, 1 << 20, 1 << 20, 0, 0, 1 << 9),  # C: 2^49 elements
+    (4, 4, 1 << 30, 1 << 30, 4, 4, 0, 0, 1 << 20),  # A: batch x M x lda > 2^48
 ])
 def test_validation_rejects(args):
     rc, _ = plan_status(*args)
     assert rc == 1
+
+
+def test_extent_limit_is_inclusive_and_shared_operands_count_once():
+    # C of 2^24 x 2^24 elements is exactly 2^48: accepted
+    rc, _ = plan_status(1 << 24, 1 << 24, 16, 16, 1 << 24, 1 << 24, 0, 0, 1)
+    assert rc == 0
+    # a shared A (batch stride 0) counts once: 2^20 batches of a 2^20 x 2^20 A pass
+    # only because A is shared (B and C are small per entry)
+    big = (1 << 20, 16, 1 << 20, 1 << 20, 16, 16, 0)
+    assert plan_status(*big, 4, 1 << 20)[0] == 0         # GEMM_A_SHARED
+    assert plan_status(*big, 0, 1 << 20)[0] == 1
 
 
 def test_noop_and_k0_plans():
