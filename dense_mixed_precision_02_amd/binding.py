@@ -204,8 +204,8 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
     acc = {GEMM_I8: torch.int32, GEMM_F64: torch.float64}.get(dt, torch.float32)
     if A.dim() not in (2, 3) or B.dim() not in (2, 3):
         raise ValueError("A and B must be 2-D or 3-D")
-    if not (A.is_cuda and B.is_cuda):
-        raise ValueError("tensors must be on the GPU")
+    if not (A.is_cuda and B.is_cuda) or B.device != A.device:
+        raise ValueError("A and B must be on the same GPU")
     M, K = A.shape[-2], A.shape[-1]
     N = B.shape[-1]
     nd = max(A.dim(), B.dim())
@@ -217,10 +217,10 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
     if C is None:
         beta = 0.0
     else:
-        if not C.is_cuda or C.dim() != nd or C.shape[-2:] != (M, N):
-            raise ValueError("C must be a GPU tensor of shape (..., M, N)")
-        if C.stride(-1) != 1:
-            raise ValueError("C must be row-major")
+        if C.device != A.device or C.dim() != nd or C.shape[-2:] != (M, N):
+            raise ValueError("C must be a tensor of shape (..., M, N) on A's GPU")
+        if C.stride(-1) != 1 or (M > 1 and C.stride(-2) < N):
+            raise ValueError("C must be row-major with a row stride of at least N")
     c_code = _out_code(C.dtype if C is not None else acc)
     if c_code is None:
         raise TypeError("C must be float32, float16, bfloat16 or int32")
@@ -239,8 +239,8 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
         strides = (M * ldc, ldc, 1) if nd == 3 else (ldc, 1)
     if out is None:
         out = torch.empty_strided(shape, strides, dtype=d_dtype, device=A.device)
-    if tuple(out.shape) != shape or out.stride() != strides:
-        raise ValueError("out must have shape (..., M, N) and C's strides")
+    if out.device != A.device or tuple(out.shape) != shape or out.stride() != strides:
+        raise ValueError("out must have shape (..., M, N) and C's strides, on A's GPU")
     if batch > 1:
         want_a = (K if a_col else M) * lda
         want_b = (N if b_col else K) * ldb
@@ -249,9 +249,10 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
             raise ValueError("batched operands must have contiguous batch strides")
     flags = (GEMM_A_COLMAJOR if a_col else 0) | (GEMM_B_COLMAJOR if b_col else 0) | \
         (GEMM_A_SHARED if a_shared else 0) | (GEMM_B_SHARED if b_shared else 0)
-    h = handle if handle is not None else default_handle()
-    stream = torch.cuda.current_stream(A.device).cuda_stream
-    h.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, out.data_ptr(),
-             M, N, K, lda, ldb, ldc, dt, flags, batch, alpha=float(alpha), beta=float(beta),
-             c_type=c_code, d_type=d_code, stream=stream)
+    with torch.cuda.device(A.device):  # the handle and the stream of A's GPU
+        h = handle if handle is not None else default_handle()
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        h.run_ex(A.data_ptr(), B.data_ptr(), C.data_ptr() if C is not None else 0, out.data_ptr(),
+                 M, N, K, lda, ldb, ldc, dt, flags, batch, alpha=float(alpha), beta=float(beta),
+                 c_type=c_code, d_type=d_code, stream=stream)
     return out

@@ -234,6 +234,27 @@ def test_torch_front_end(handle):
     assert torch.equal(D8.cpu().long(), ref8)
 
 
+def test_torch_front_end_rejects(handle):
+    """Layouts the C ABI cannot express raise before anything is launched."""
+    import dense_mixed_precision_02_amd as dmp
+    A = torch.zeros(64, 32, dtype=torch.float16, device="cuda")
+    B = torch.zeros(32, 48, dtype=torch.float16, device="cuda")
+    C = torch.zeros(64, 48, device="cuda")
+    bad = [
+        lambda: dmp.gemm(A, B, torch.zeros(1, 48, device="cuda").expand(64, 48)),  # row stride 0
+        lambda: dmp.gemm(A, B, C.t().contiguous().t()),                          # column-major C
+        lambda: dmp.gemm(A, B, C[:, :47]),                                        # shape
+        lambda: dmp.gemm(A, B.float(), C),                                        # dtype
+        lambda: dmp.gemm(A, B, C.cpu()),                                          # device
+        lambda: dmp.gemm(A[:, ::2], B[:16], C),                                   # strided k
+        lambda: dmp.gemm(A, B, C, out=torch.empty(64, 48, device="cuda")[:, :47]),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises((ValueError, TypeError)):
+            f()
+    torch.cuda.synchronize()
+
+
 def test_int8_transposed_b_path(handle):
     """Large-M int8 with row-major B goes through a transposed copy of B; ragged N and
     K (multiples of 16) exercise the copy's edges, and a batch its batch stride."""
