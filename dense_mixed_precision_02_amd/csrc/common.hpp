@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "epi.hpp"
+
 namespace dmp {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -123,20 +125,9 @@ __device__ static inline int32_t add_acc(int32_t a, int32_t b) {
 }
 
 // ---------------------------------------------------------------------------
-// Output stage.  D = cvt_D(alpha * acc + beta * cvt_C(C)) with every step an
-// fp32 round-to-nearest-even operation (no fused multiply-add), C decoded
-// exactly from its storage type and the final conversion to D's storage type
-// rounding to nearest even.  alpha = beta = 1 with fp32 C and D is the plain
-// D = acc + C.  The int8 path only has D = acc + C (int32, wrapping) or D = acc.
+// Output stage (parameters and semantics in epi.hpp): loads and stores of C and
+// D in their storage types, and the alpha/beta combination.
 // ---------------------------------------------------------------------------
-enum { OUT_F32 = 0, OUT_F16 = 1, OUT_BF16 = 2, OUT_I32 = 3, OUT_F64 = 4 };
-
-struct EpiParams {
-    float alpha, beta;
-    int c_type, d_type;
-    int use_c;  // beta != 0: C is read
-};
-
 __device__ static inline int out_size(int t) {
     return (t == OUT_F16 || t == OUT_BF16) ? 2 : t == OUT_F64 ? 8 : 4;
 }

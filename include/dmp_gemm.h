@@ -55,9 +55,10 @@
  *
  * Errors: every call returns a gemm_status_t.  Arguments are validated before
  * anything is enqueued; on error nothing is launched.  Limits: M, N, K below
- * 2^31 - 1024, batch at most 2^30, and every operand's extent (the largest
- * element index over all batch entries, from the leading dimensions and batch
- * strides) at most 2^48 elements; beyond them GEMM_ERR_INVALID_ARG.  Launches
+ * 2^31 - 1024, batch at most 2^30, leading dimensions at most 2^48, and
+ * every operand's extent (the largest element index over all batch entries,
+ * from the leading dimensions and batch strides) at most 2^48 elements;
+ * beyond them GEMM_ERR_INVALID_ARG.  Launches
  * are asynchronous on `stream` (a hipStream_t, NULL = the null stream), so
  * faults during execution surface at the caller's next synchronisation.
  */

@@ -71,6 +71,7 @@ def plan_status(*args):
     (4, 4, 8, 8, 4, 1 << 62, 0, 0, 1),     # ldc beyond 2^48 elements
     (1 << 20, 1 << 20, 8, 8, 1 << 20, 1 << 20, 0, 0, 1 << 9),  # C: 2^49 elements
     (4, 4, 1 << 30, 1 << 30, 4, 4, 0, 0, 1 << 20),  # A: batch x M x lda > 2^48
+    (1, 4, 8, (1 << 48) + 1, 4, 4, 0, 0, 1),  # one-row A: its lda alone beyond 2^48
 ])
 def test_validation_rejects(args):
     rc, _ = plan_status(*args)
