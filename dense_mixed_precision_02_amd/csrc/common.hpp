@@ -115,6 +115,22 @@ __device__ static inline void barrier_vmcnt() {
     asm volatile("" ::: "memory");
 }
 
+// Race check.  A build with DMP_EXTRA_SYNC defined waits for every copy and
+// meets every wave at each step of the software pipelines (step_sync() is
+// empty otherwise); the arithmetic is unchanged, so its results must equal the
+// normal build's bit for bit, whatever the timing of copies and reads.
+#ifdef DMP_EXTRA_SYNC
+constexpr bool EXTRA_SYNC = true;
+#else
+constexpr bool EXTRA_SYNC = false;
+#endif
+__device__ static inline void step_sync() {
+    if constexpr (EXTRA_SYNC) {
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
+}
+
 // C is added once after the reduction: an fp32 round-to-nearest-even add, or an
 // int32 add that wraps modulo 2^32 (done in unsigned arithmetic, where wrapping
 // is defined).

@@ -205,10 +205,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         __syncthreads();
         for (int kt = 0; kt < ntiles; kt += 2) {
             stage(kt + 1, la1, lb1);
+            step_sync();
             compute(la0, lb0);
             wait_vmcnt<0>();
             __syncthreads();
             stage(kt + 2, la0, lb0);  // past the last k-tile: zero fill only
+            step_sync();
             compute(la1, lb1);
             wait_vmcnt<0>();
             __syncthreads();

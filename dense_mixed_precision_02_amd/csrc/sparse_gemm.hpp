@@ -272,11 +272,13 @@ __global__ __launch_bounds__(256) void sparse_gemm(const SparseArgs p) {
         mma(F0);
         interleave<NMF, NRD, NL>();
         __builtin_amdgcn_sched_barrier(0);
+        step_sync();
         barrier_vmcnt<NL>();  // k-tile tt+1 has landed everywhere; tt+2 may still be in flight
         read(F0, LA[n], LM[n], LB[n], 0);
         mma(F1);
         interleave<NMF, NRD, 0>();
         __builtin_amdgcn_sched_barrier(0);
+        step_sync();
     };
     if (p.nkt > 0) {
         stage(0, LA[0], LM[0], LB[0]);

@@ -308,11 +308,13 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         mma(fa0, fb0);
         interleave<NMF, NRD, P2 - P1>();
         __builtin_amdgcn_sched_barrier(0);
+        step_sync();
         // step 1
         read(fa0, fb0, la, lb, 2);
         mma(fa1, fb1);
         interleave<NMF, NRD, 0>();
         __builtin_amdgcn_sched_barrier(0);
+        step_sync();
         // step 2
         read(fa1, fb1, la, lb, 3);
         mma(fa0, fb0);
@@ -326,6 +328,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         mma(fa1, fb1);
         interleave<NMF, NRD, P1>();
         __builtin_amdgcn_sched_barrier(0);
+        step_sync();
     };
     if (nkt > 0) {
         stage_part(0, LA[0], LB[0], Z{}, I2{});
