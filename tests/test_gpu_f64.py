@@ -3,6 +3,8 @@
 Per element |D - D_ref| <= (2K+2)*2^-53*S + 2^-53*|c| (the fp64 instruction
 rounds every step to nearest even); inputs whose every partial sum is an
 integer below 2^53 must match bit for bit."""
+from fractions import Fraction
+
 import numpy as np
 import pytest
 
@@ -226,3 +228,56 @@ def test_torch_front_end(handle):
     out = dmp.gemm(A, Bt.t(), C)
     assert out.dtype == torch.float64
     check_full(p, out[None])
+
+
+def _rne_inputs(M, K, rng):
+    """A (M x K) with full 52-bit mantissas and the diagonal d of B, plus two
+    exact ties in row 0: (1 + 2^-52)*1.5 sits halfway between 1.5 + 2^-52 (odd
+    last bit) and 1.5 + 2^-51 (even), (1 + 3*2^-52)*1.5 halfway between
+    1.5 + 4*2^-52 (even) and 1.5 + 5*2^-52 (odd)."""
+    A = np.ldexp(1.0 + rng.integers(0, 1 << 52, size=(M, K)) * 2.0 ** -52,
+                 rng.integers(-20, 21, size=(M, K))) * rng.choice([-1.0, 1.0], size=(M, K))
+    d = np.ldexp(1.0 + rng.integers(0, 1 << 52, size=K) * 2.0 ** -52, rng.integers(-20, 21, size=K))
+    A[0, 0], A[0, 1] = 1.0 + 2.0 ** -52, 1.0 + 3 * 2.0 ** -52
+    d[0] = d[1] = 1.5
+    return A, d
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (2048, 2048), (37, 37)],
+                         ids=["dtile64", "dtile128", "dgeneric"])
+def test_products_round_to_nearest_even(handle, shape):
+    """The fp64 matrix instruction rounds products to nearest, ties to even (the
+    FP64-accumulate builtins section of the CDNA2 dense MFMA builtins page; round
+    toward zero is what it does not do).  With B = diag(d) every output holds one
+    nonzero product and every other step adds an exact zero, so D_ij must be
+    exactly the correctly rounded a_ij * d_j, which numpy's fp64 product is.
+    Round toward zero would miss about half of the elements and both ties; round
+    half away from zero would miss the second tie."""
+    import dense_mixed_precision_02_amd as dmp
+    M, K = shape
+    rng = np.random.default_rng(91)
+    A, d = _rne_inputs(M, K, rng)
+    B = np.diag(d)
+    want = A * d[None, :]
+    assert want[0, 0] == 1.5 + 2.0 ** -51 and want[0, 1] == 1.5 + 4 * 2.0 ** -52
+    for i, j in [(0, 0), (0, 1), (1, 2), (M - 1, K - 1)]:
+        assert want[i, j] == float(Fraction(A[i, j]) * Fraction(d[j]))
+    label = dmp.plan_label(M, K, K, K, K, K, F64, 0).split()[0]
+    log(f"[f64-rne] {M}x{K}x{K} path {label}")
+    Ad, Bd = dev(A), dev(B)
+    C = torch.zeros((M, K), dtype=torch.float64, device="cuda")
+    D = torch.empty_like(C)
+    handle.run(Ad.data_ptr(), Bd.data_ptr(), C.data_ptr(), D.data_ptr(), M, K, K, K, K, K, F64, 0, 1,
+               torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = D.cpu().numpy()
+    assert got[0, 0] == want[0, 0] and got[0, 1] == want[0, 1], "ties not rounded to even"
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} products not rounded to nearest, first at {bad[0]}"
+
+
+def test_rne_shapes_reach_every_fp64_path():
+    import dense_mixed_precision_02_amd as dmp
+    seen = {dmp.plan_label(M, K, K, K, K, K, F64, 0).split()[0] for M, K in
+            [(256, 256), (2048, 2048), (37, 37)]}
+    assert seen == {"dtile64x64", "dtile128x128", "dgeneric16x16"}, seen
