@@ -8,8 +8,11 @@ already resident in HBM.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C2] [--no-cpu]
 
---config picks another workload of the same family (C1, C3, C4, C5, S1) for the
-documentation tables; the graded line is the default one.  --d-type / --c-type /
+--config picks another workload (C1, C3, C4, C5, S1; F1 fp64; SP1, SP2 with a
+2:4-sparse A; T1 tiny batched products); the headline line is the default one.
+--rotate N times the steps over N device copies of the operands (default 2 for
+the bandwidth-bound C4, C5 and T1), so no step finds its inputs in the
+memory-side cache.  --d-type / --c-type /
 --alpha / --beta time the scaled, converted output stage instead
 (D = cvt_D(alpha*A*B + beta*C) through gemm_run_ex; --c-type none means beta = 0
 and no C read).
