@@ -48,7 +48,18 @@ ROTATE_SETS = 2
 METRIC = "GEMM TFLOPS/TOPS (fp16, bf16, int8) on 1 MI355X; % of dense MFMA peak"
 COPY_BYTES = 512 << 20
 # rocprofv3 HBM-traffic summary of the dominant kernel of each workload
-TRAFFIC_FILES = {"C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md"}
+TRAFFIC_FILES = {
+    "C1": "profiles/tile_gemm_f16_256x256x256_traffic.md",
+    "C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md",
+    "C3": "profiles/tile_gemm_i8_8192x8192x8192_traffic.md",
+    "C4": "profiles/tile_gemm_f16_batch8192_64x64x64_traffic.md",
+    "C5": "profiles/tile_gemm_splitk_bf16_1024x1024x65536_traffic.md",
+    "S1": "profiles/tile_gemm_f16_4096x4096x4096_traffic.md",
+    "F1": "profiles/dgemm_tile_f64_4096x4096x4096_traffic.md",
+    "SP1": "profiles/sparse_gemm_bf16_4096x4096x4096_traffic.md",
+    "SP2": "profiles/sparse_gemm_i8_8192x8192x8192_traffic.md",
+    "T1": "profiles/tiny_gemm_f16_batch1048576_4x4x16_traffic.md",
+}
 
 
 OUT_SIZE = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4, "none": 0}

@@ -23,15 +23,19 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["dense_mixed_precision_02_amd/csrc/common.hpp",
-                  "dense_mixed_precision_02_amd/csrc/tile_gemm.hpp",
-                  "dense_mixed_precision_02_amd/csrc/aux_kernels.hpp",
-                  "dense_mixed_precision_02_amd/csrc/gemm_api.hip"]
+CSRC = "dense_mixed_precision_02_amd/csrc"
+
+
+def kernel_sources() -> list:
+    """Every source the library is built from (kernels, path selection, the C ABI)."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                  if f.endswith((".hpp", ".hip", ".h")))
 
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources():
+        h.update(rel.encode())
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -25,6 +25,21 @@ def test_more_than_one_gpu_is_refused(capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
+def test_every_workload_has_a_traffic_summary():
+    """Each workload names a rocprofv3 FETCH_SIZE/WRITE_SIZE summary under profiles/
+    that parses and states a source hash; every config is covered."""
+    import os
+    import bench_profile
+    assert set(bench.TRAFFIC_FILES) == set(synth.CONFIGS)
+    for name, rel in bench.TRAFFIC_FILES.items():
+        path = os.path.join(bench.ROOT, rel)
+        assert os.path.exists(path), rel
+        nbytes, digest = bench_profile.read_traffic(path)
+        assert nbytes > 0 and len(digest) == 16, rel
+        text = open(path).read()
+        assert f"--config {name} " in text, rel
+
+
 def test_algorithmic_bytes():
     p = synth.make_problem("f16", 64, 64, 64, batch=8192, seed=4)
     # A + B (2 bytes) read once, C (fp32) read once, D (fp32) written once
