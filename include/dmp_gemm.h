@@ -53,6 +53,14 @@
  * would share the workspace).  D may alias C exactly (same pointer, same ldc); any other overlap
  * between D and an input is undefined.
  *
+ * Graph capture: the calls enqueue kernels only (no memset or copy nodes), so
+ * they can be captured into a HIP graph once the handle's workspace is large
+ * enough, i.e. after an eager call of the same (or a larger) shape on the same
+ * handle; a call that must grow the workspace synchronises the device and
+ * allocates, which capture does not allow.  A graph keeps the workspace's
+ * address: replaying it after a later call on the handle has grown (replaced)
+ * the workspace is undefined.
+ *
  * Errors: every call returns a gemm_status_t.  Arguments are validated before
  * anything is enqueued; on error nothing is launched.  Limits: M, N, K below
  * 2^31 - 1024, batch at most 2^30, leading dimensions at most 2^48, and
