@@ -125,3 +125,58 @@ def test_results_beyond_int32_wrap(handle, shape):
     torch.cuda.synchronize()
     got = D.cpu().numpy().astype(np.int64).reshape(batch, M, p.ldc)[:, :, :N]
     assert np.array_equal(got, wrap32(exact))
+
+
+def test_sparse_partial_sums_beyond_int32_final_exact(handle):
+    """The 2:4 int8 product: A holds a_i at k = 0, 1 (mod 4) and zeros at k = 2, 3,
+    so the compressor keeps exactly the a_i entries; with c_j = #{k < h_j : k mod 4 < 2}
+    D_ij = C_ij + a_i (127 K/2 - 255 c_j), and a running sum of a row with
+    a_i = -128 passes 2^31 once c_j > 131072."""
+    from test_gpu_sparse import compress, run_sparse
+    M = N = 512
+    K = 786432
+    rng = np.random.default_rng(95)
+    a = rng.integers(-128, 128, size=M).astype(np.int64)
+    a[0], a[-1] = -128, 127
+    L = ((1 << 31) - (1 << 21)) // 128
+    cmax = (127 * K // 2 + L) // 255
+    h = rng.integers(2 * 131073 + 4, 2 * cmax - 4, size=N).astype(np.int64)
+    cnt = 2 * (h // 4) + np.minimum(h % 4, 2)
+    assert cnt.min() > 131072 and cnt.max() <= cmax
+    A = np.zeros((1, M, K), dtype=np.int8)
+    A[0, :, 0::4] = a[:, None].astype(np.int8)
+    A[0, :, 1::4] = a[:, None].astype(np.int8)
+    Bnk = np.full((1, N, K), 127, dtype=np.int8)
+    for j in range(N):
+        Bnk[0, j, :h[j]] = -128
+    C = rng.integers(-(1 << 20), 1 << 20, size=(1, M, N)).astype(np.int32)
+    want = C.astype(np.int64) + a[None, :, None] * (127 * K // 2 - 255 * cnt[None, None, :])
+    assert np.all(np.abs(want) < (1 << 31))
+    p = synth.Problem("i8", M, N, K, 1, K, K, N, False, True, A, Bnk, C)
+    pts = np.array([(0, i, j) for i in (0, 100, M - 1) for j in (0, 7, N - 1)], dtype=np.int64)
+    pruned = oracle.prune24("i8", A[:, :, :4096], M, 4096, 4096, 1)
+    assert np.array_equal(pruned, A[:, :, :4096]), "the compressor keeps the a_i entries"
+    assert np.array_equal(oracle.gemm_points("i8", A, Bnk, C, pts, **p.oracle_args()),
+                          want[0][pts[:, 1], pts[:, 2]])
+    log(f"[int-wrap] sparse {M}x{N}x{K}")
+    Ac, meta = compress(handle, p)
+    got = run_sparse(handle, p, Ac, meta).astype(np.int64)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[0]}"
+
+
+def test_sparse_results_beyond_int32_wrap(handle):
+    from test_gpu_sparse import compress, run_sparse
+    M, N, K = 256, 256, 256
+    p = synth.make_problem("i8", M, N, K, b_col=True, seed=96)
+    rng = np.random.default_rng(97)
+    off = rng.integers(0, 1 << 13, size=(1, M, N))
+    C = np.where(np.arange(M)[None, :, None] < M // 2, (1 << 31) - 1 - off, -(1 << 31) + off)
+    p.C[...] = C.astype(np.int32)
+    pruned = oracle.prune24("i8", p.A, M, K, p.lda, 1)
+    exact = oracle.gemm("i8", pruned, p.B, p.C, **p.oracle_args())
+    assert np.mean(np.abs(exact) >= (1 << 31)) > 0.25
+    log(f"[int-wrap] sparse final {M}x{N}x{K}")
+    Ac, meta = compress(handle, p)
+    got = run_sparse(handle, p, Ac, meta).astype(np.int64).reshape(1, M, p.ldc)[:, :, :N]
+    assert np.array_equal(got, wrap32(exact))
