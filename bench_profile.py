@@ -149,6 +149,16 @@ def cmd_counters(a):
         if "TCP_PENDING_STALL_CYCLES_sum" in med:
             lines.append(f"L1 stalled on pending L2 data: "
                          f"{100 * med['TCP_PENDING_STALL_CYCLES_sum'] / 256 / cyc:.1f} % of cycles per CU")
+    if "SQ_LDS_IDX_ACTIVE" in med and med["SQ_LDS_IDX_ACTIVE"] > 0:
+        act = med["SQ_LDS_IDX_ACTIVE"]
+        for n, what in (("SQ_LDS_BANK_CONFLICT", "bank-conflict"), ("SQ_LDS_ADDR_CONFLICT", "address-conflict"),
+                        ("SQ_LDS_UNALIGNED_STALL", "unaligned-stall"), ("SQ_LDS_DATA_FIFO_FULL", "data-FIFO-full")):
+            if n in med:
+                lines.append(f"LDS {what} cycles per LDS-active cycle ({n} / SQ_LDS_IDX_ACTIVE): "
+                             f"{100 * med[n] / act:.2f} %")
+    if "SQ_INSTS_LDS" in med and med.get("SQ_WAVES"):
+        lines.append(f"LDS instructions per wave: {med['SQ_INSTS_LDS'] / med['SQ_WAVES']:.0f} "
+                     f"({med['SQ_WAVES']:.0f} waves)")
     if "TCC_HIT_sum" in med and "TCC_MISS_sum" in med:
         h, m = med["TCC_HIT_sum"], med["TCC_MISS_sum"]
         lines.append(f"L2 hit rate: {100 * h / (h + m):.1f} %")
