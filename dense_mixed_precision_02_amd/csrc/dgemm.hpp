@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             const int64_t row = m0 + wm * WTM + i * 16 + r;
             if (row < p.M && col < p.N) {
                 const int64_t idx = row * p.ldc + col;
-                Db[idx] = p.use_c ? v + Cb[idx] : v;
+                __builtin_nontemporal_store(p.use_c ? v + Cb[idx] : v, Db + idx);  // D is written once
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(64) void dgemm_generic(const DgemmArgs p, int a_col
         const int64_t r = m0 + 4 * G + q;
         if (r < p.M && c < p.N) {
             const int64_t idx = r * p.ldc + c;
-            Db[idx] = p.use_c ? acc[G] + Cb[idx] : acc[G];
+            __builtin_nontemporal_store(p.use_c ? acc[G] + Cb[idx] : acc[G], Db + idx);
         }
     }
 }
