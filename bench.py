@@ -10,7 +10,7 @@ already resident in HBM.  Prints ONE JSON line.
 
 --config picks another workload (C1, C3, C4, C5, S1; F1 fp64; SP1, SP2 with a
 2:4-sparse A; T1 tiny batched products); the headline line is the default one.
---rotate N times the steps over N device copies of the operands (default 2 for
+--rotate N times the steps over N device copies of the operands (default 4 for
 the bandwidth-bound C4, C5 and T1), so no step finds its inputs in the
 memory-side cache.  --d-type / --c-type /
 --alpha / --beta time the scaled, converted output stage instead
@@ -40,11 +40,14 @@ DTYPE_CODE = {"f16": 0, "bf16": 1, "i8": 2, "f64": 3}
 # intensity below the ~315 FLOP/byte ridge).
 HBM_BOUND = {"C4", "T1"}
 # Configs whose HBM traffic matters: the timed steps rotate over ROTATE_SETS
-# device copies of the operands and outputs, so that a step never finds the
-# previous step's data in the 256 MB memory-side cache (each config's
-# footprint is above 256 MB, two sets above 512 MB).
+# device copies of the operands and outputs, so that a step does not find its
+# inputs in the 256 MB memory-side cache.  D is stored non-temporally and does
+# not enter that cache, so what must exceed it is the inputs read (A, B, C):
+# 268 MB per set for the batched 64^3 products.  Two such sets still gave 18 %
+# cache hits in time (62 against 75.5 us per step); three and four sets gave
+# the same 75.5 us.  Four sets put every rotated workload's reads above 1 GB.
 ROTATE = {"C4", "C5", "T1"}
-ROTATE_SETS = 2
+ROTATE_SETS = 4
 METRIC = "GEMM TFLOPS/TOPS (fp16, bf16, int8) on 1 MI355X; % of dense MFMA peak"
 COPY_BYTES = 512 << 20
 # rocprofv3 HBM-traffic summary of the dominant kernel of each workload
