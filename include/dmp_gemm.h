@@ -53,6 +53,11 @@
  * would share the workspace).  D may alias C exactly (same pointer, same ldc); any other overlap
  * between D and an input is undefined.
  *
+ * Caching: D (every output the library writes) is stored with non-temporal
+ * stores.  It is written once and is not kept in the caches, so it does not
+ * displace operands; a kernel that reads D right afterwards fetches it from
+ * HBM.
+ *
  * Graph capture: the calls enqueue kernels only (no memset or copy nodes), so
  * they can be captured into a HIP graph once the handle's workspace is large
  * enough, i.e. after an eager call of the same (or a larger) shape on the same
@@ -112,8 +117,8 @@ int gemm_create(gemm_handle_t *out);
  * A, B, C, D: device pointers (must be non-NULL when the product is non-empty).
  * M, N, K, batch >= 0.  M, N or batch == 0 is a no-op returning GEMM_OK.
  * K == 0 gives D = C (A, B and their leading dimensions are then not used).
- * dtype: a gemm_dtype_t.  flags: GEMM_A_COLMAJOR |
- * GEMM_B_COLMAJOR.  Pointers must be aligned to their element size; any such
+ * dtype: a gemm_dtype_t.  flags: any OR of GEMM_A_COLMAJOR, GEMM_B_COLMAJOR,
+ * GEMM_A_SHARED and GEMM_B_SHARED.  Pointers must be aligned to their element size; any such
  * pointer and any leading dimension is accepted, and 16-byte aligned pointers
  * with leading dimensions that are multiples of 16 bytes take the fast tiled
  * path (for K-contiguous operands K, for M/N-contiguous ones M or N, must also
