@@ -30,7 +30,10 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b16 __attribute__((ext_vector_type(16)));
 
 enum { P_F16_32 = 0, P_BF16_32 = 1, P_I8_32 = 2, P_SP_BF16_32 = 3, P_SP_I8_32 = 4,
-       P_F64_16 = 5, P_F16_4X4 = 6, P_F16_16X4 = 7, P_COUNT = 8 };
+       P_F64_16 = 5, P_F16_4X4 = 6, P_F16_16X4 = 7, P_BF16_4X4 = 8, P_BF16_16X4 = 9,
+       P_I8_4X4 = 10, P_I8_16X4 = 11, P_COUNT = 12 };
+
+typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 
 constexpr int REGS = 16;  // registers written per lane (unused ones are zero)
 
@@ -91,20 +94,41 @@ __global__ __launch_bounds__(64) void probe_f64(double *out) {
     put(out, acc, 4);
 }
 
-// S x S blocks, 64 / S of them: combo c = (b * S + i) * S + j
-template <int S>
+// S x S blocks, 64 / S of them: combo c = (b * S + i) * S + j.  T: 0 fp16,
+// 1 bf16 (the _1k instructions), 2 int8; four k per lane in every case.
+template <int S, int T>
 __global__ __launch_bounds__(64) void probe_multi(double *out) {
     const int c = blockIdx.x, j = c % S, i = (c / S) % S, b = c / (S * S), L = threadIdx.x;
-    const uint64_t ones = ((uint64_t)F16_ONE2 << 32) | F16_ONE2;
+    const uint32_t one2 = T == 0 ? F16_ONE2 : BF16_ONE2;
+    const uint64_t ones = ((uint64_t)one2 << 32) | one2;
     const uint64_t a = L == b * S + i ? ones : 0, bb = L == b * S + j ? ones : 0;
+    const int a8 = L == b * S + i ? (int)I8_ONE4 : 0, b8v = L == b * S + j ? (int)I8_ONE4 : 0;
     if constexpr (S == 4) {
-        floatx4 acc = {};
-        acc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, bb), acc, 0, 0, 0);
-        put(out, acc, 4);
+        if constexpr (T == 2) {
+            intx4 acc = {};
+            acc = __builtin_amdgcn_mfma_i32_4x4x4i8(a8, b8v, acc, 0, 0, 0);
+            put(out, acc, 4);
+        } else {
+            floatx4 acc = {};
+            if constexpr (T == 0)
+                acc = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, bb), acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(b4, a), __builtin_bit_cast(b4, bb), acc, 0, 0, 0);
+            put(out, acc, 4);
+        }
     } else {
-        floatx16 acc = {};
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, bb), acc, 0, 0, 0);
-        put(out, acc, 16);
+        if constexpr (T == 2) {
+            intx16 acc = {};
+            acc = __builtin_amdgcn_mfma_i32_16x16x4i8(a8, b8v, acc, 0, 0, 0);
+            put(out, acc, 16);
+        } else {
+            floatx16 acc = {};
+            if constexpr (T == 0)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f16(__builtin_bit_cast(h4, a), __builtin_bit_cast(h4, bb), acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_16x16x4bf16_1k(__builtin_bit_cast(b4, a), __builtin_bit_cast(b4, bb), acc, 0, 0, 0);
+            put(out, acc, 16);
+        }
     }
 }
 
@@ -115,8 +139,8 @@ int mfma_probe_combos(int which) {
     switch (which) {
         case P_F16_32: case P_BF16_32: case P_I8_32: case P_SP_BF16_32: case P_SP_I8_32: return 32 * 32;
         case P_F64_16: return 16 * 16;
-        case P_F16_4X4: return 16 * 4 * 4;
-        case P_F16_16X4: return 4 * 16 * 16;
+        case P_F16_4X4: case P_BF16_4X4: case P_I8_4X4: return 16 * 4 * 4;
+        case P_F16_16X4: case P_BF16_16X4: case P_I8_16X4: return 4 * 16 * 16;
         default: return 0;
     }
 }
@@ -135,8 +159,12 @@ int mfma_probe_run(int which, double *out, void *stream) {
         case P_SP_BF16_32: hipLaunchKernelGGL(probe_32<P_SP_BF16_32>, dim3(n), dim3(64), 0, s, out); break;
         case P_SP_I8_32: hipLaunchKernelGGL(probe_32<P_SP_I8_32>, dim3(n), dim3(64), 0, s, out); break;
         case P_F64_16: hipLaunchKernelGGL(probe_f64, dim3(n), dim3(64), 0, s, out); break;
-        case P_F16_4X4: hipLaunchKernelGGL(probe_multi<4>, dim3(n), dim3(64), 0, s, out); break;
-        case P_F16_16X4: hipLaunchKernelGGL(probe_multi<16>, dim3(n), dim3(64), 0, s, out); break;
+        case P_F16_4X4: hipLaunchKernelGGL((probe_multi<4, 0>), dim3(n), dim3(64), 0, s, out); break;
+        case P_F16_16X4: hipLaunchKernelGGL((probe_multi<16, 0>), dim3(n), dim3(64), 0, s, out); break;
+        case P_BF16_4X4: hipLaunchKernelGGL((probe_multi<4, 1>), dim3(n), dim3(64), 0, s, out); break;
+        case P_BF16_16X4: hipLaunchKernelGGL((probe_multi<16, 1>), dim3(n), dim3(64), 0, s, out); break;
+        case P_I8_4X4: hipLaunchKernelGGL((probe_multi<4, 2>), dim3(n), dim3(64), 0, s, out); break;
+        case P_I8_16X4: hipLaunchKernelGGL((probe_multi<16, 2>), dim3(n), dim3(64), 0, s, out); break;
     }
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }

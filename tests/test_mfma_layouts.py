@@ -82,6 +82,10 @@ PROBES = [
     (5, "16x16f64", 4, "mfma_f64_16x16x4f64"),
     (6, "4x4", 4, "mfma_f32_4x4x4f16 (16 blocks)"),
     (7, "16x16", 4, "mfma_f32_16x16x4f16 (4 blocks)"),
+    (8, "4x4", 4, "mfma_f32_4x4x4bf16_1k (16 blocks)"),
+    (9, "16x16", 4, "mfma_f32_16x16x4bf16_1k (4 blocks)"),
+    (10, "4x4", 4, "mfma_i32_4x4x4i8 (16 blocks)"),
+    (11, "16x16", 4, "mfma_i32_16x16x4i8 (4 blocks)"),
 ]
 
 
