@@ -157,3 +157,38 @@ def test_sweep_reached_every_path():
                  "tiny16x16x4b", "dtile64x64", "dgeneric16x16", "copy",
                  "tile256x256 split", "tile64x64 split"):
         assert any(x.startswith(need) for x in PATHS), (need, sorted(PATHS))
+
+
+SP_CHUNKS, SP_PER_CHUNK = 4, 30
+
+
+@pytest.mark.parametrize("chunk", range(SP_CHUNKS))
+def test_random_sparse_sweep_against_the_oracle(handle, chunk):
+    """The 2:4 path: random type, sizes, batch, B layout and padding (B's leading
+    dimension stays a whole number of 16-byte granules, as the entry point
+    requires); the compressed form must equal the one built from the oracle's
+    kept positions, and the product the oracle's product of the pruned A."""
+    from test_gpu_sparse import check, compress, expected_compressed, run_sparse, same_compressed
+    rng = np.random.default_rng(3030 + chunk)
+    for n in range(chunk * SP_PER_CHUNK, (chunk + 1) * SP_PER_CHUNK):
+        dt = ["f16", "bf16", "i8"][rng.integers(3)]
+        gran = 16 if dt == "i8" else 8
+        b_col = bool(rng.integers(2))
+        M = int(rng.choice(DIMS + BIG[:2]))
+        N = int(rng.choice(DIMS + BIG[:2]))
+        K = int(rng.choice(KS + KS_ALIGNED[:6]))
+        if b_col:
+            K = max(gran, (K + gran - 1) // gran * gran)
+        else:
+            N = max(gran, (N + gran - 1) // gran * gran)
+        batch = int(rng.integers(1, 4))
+        if M * N * K * batch > MAX_MACS:
+            K = max(gran * 8, int(MAX_MACS // (M * N * batch)) // (gran * 8) * (gran * 8))
+        pad = int(rng.choice([0, gran]))
+        kw = dict(c_range=(-(1 << 20), 1 << 20)) if dt == "i8" else {}
+        p = synth.make_problem(dt, M, N, K, batch=batch, b_col=b_col, pad=pad, seed=7000 + n, **kw)
+        log(f"[sparse sweep {n}] {dt} {batch} x {M}x{N}x{K} b_col={b_col} pad={pad}")
+        Ac, meta = compress(handle, p)
+        pruned, eAc, emeta = expected_compressed(p)
+        assert same_compressed(p, Ac, meta, eAc, emeta), f"case {n}: compressed form"
+        check(p, pruned, run_sparse(handle, p, Ac, meta))
