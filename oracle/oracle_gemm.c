@@ -5,8 +5,8 @@
  * does, and the two share no code.
  *
  * What it follows (pages: "CDNA2 dense MFMA builtins", section "Naming
- * convention"; "RDNA3 dense WMMA builtins", builtin reference "Returns ...
- * updated accumulator"): one multiply-accumulate step adds the contribution of
+ * convention"; "RDNA3 dense WMMA builtins", builtin reference, where each
+ * builtin yields the new accumulator): one multiply-accumulate step adds the contribution of
  * a K-wide panel of A (M x K) and of B (K x N) to an M x N tile, and the full
  * product is the sum over all K panels, plus the accumulator input C.  The
  * oracle does not split K into panels at all: the plain definition
