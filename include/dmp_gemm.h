@@ -2,10 +2,10 @@
  * dmp_gemm.h -- C ABI of the gfx950 (MI355X) dense mixed-precision GEMM library.
  *
  * Operation (pages: "CDNA2 dense MFMA builtins", section "Naming convention",
- * and "RDNA3 dense WMMA builtins", builtin reference): one MFMA step adds the
- * contribution of a K-wide panel of A (M x K) and of B (K x N) to an M x N
- * accumulator tile; the caller loops over K and the result of a step is
- * srcA x srcB + srcC.  This library runs the whole loop on the GPU and computes,
+ * and "RDNA3 dense WMMA builtins", builtin reference): one MFMA step multiplies
+ * a slice of A (M rows, a few k) by the matching slice of B (same k, N columns)
+ * and adds the result into an M x N accumulator tile, srcA x srcB + srcC; the
+ * caller steps through all of K.  This library runs the whole loop on the GPU and computes,
  * for every batch index b < batch,
  *
  *         D_b = A_b * B_b + C_b

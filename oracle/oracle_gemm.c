@@ -6,9 +6,10 @@
  *
  * What it follows (pages: "CDNA2 dense MFMA builtins", section "Naming
  * convention"; "RDNA3 dense WMMA builtins", builtin reference, where each
- * builtin yields the new accumulator): one multiply-accumulate step adds the contribution of
- * a K-wide panel of A (M x K) and of B (K x N) to an M x N tile, and the full
- * product is the sum over all K panels, plus the accumulator input C.  The
+ * builtin yields the new accumulator): one multiply-accumulate step multiplies a
+ * slice of A (M rows, a few k) by the matching slice of B (same k, N columns)
+ * and adds it into an M x N tile, so the full product is the sum over all k
+ * slices, plus the accumulator input C.  The
  * oracle does not split K into panels at all: the plain definition
  *
  *     D[b][i][j] = x(C[b][i][j]) + sum_k x(A[b][i][k]) * x(B[b][k][j])
