@@ -102,7 +102,9 @@ typedef enum {
     GEMM_ERR_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad dtype/flags */
     GEMM_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950; there is no fallback */
     GEMM_ERR_ALLOC = 3,              /* workspace allocation failed */
-    GEMM_ERR_HIP = 4                 /* a HIP API call or kernel launch reported an error */
+    GEMM_ERR_HIP = 4                 /* a HIP API call or kernel launch reported an error; the
+                                        launch status is read with hipGetLastError, so an error an
+                                        earlier HIP call of this thread left unread is reported too */
 } gemm_status_t;
 
 /*
