@@ -256,3 +256,82 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
                  M, N, K, lda, ldb, ldc, dt, flags, batch, alpha=float(alpha), beta=float(beta),
                  c_type=c_code, d_type=d_code, stream=stream)
     return out
+
+
+class Sparse24:
+    """A 2:4-compressed A (the library's blocked form): values ``Ac``, index words
+    ``meta``, and the dense sizes M, K, the input code and the batch."""
+
+    def __init__(self, Ac, meta, M: int, K: int, dtype: int, batch: int):
+        self.Ac, self.meta, self.M, self.K, self.dtype, self.batch = Ac, meta, M, K, dtype, batch
+
+
+def prune24(A, handle: Handle | None = None) -> Sparse24:
+    """Compress A ((batch,) M, K; float16, bfloat16 or int8; rows K-contiguous with
+    contiguous batches) to 2:4 form on the current stream: in every group of four
+    consecutive k of a row the two entries of largest magnitude are kept."""
+    import torch
+    dt = {torch.float16: GEMM_F16, torch.bfloat16: GEMM_BF16, torch.int8: GEMM_I8}.get(A.dtype)
+    if dt is None:
+        raise TypeError("A must be float16, bfloat16 or int8")
+    if A.dim() not in (2, 3) or not A.is_cuda:
+        raise ValueError("A must be a 2-D or 3-D GPU tensor")
+    M, K = A.shape[-2], A.shape[-1]
+    batch = A.shape[0] if A.dim() == 3 else 1
+    if A.stride(-1) != 1 or (M > 1 and A.stride(-2) < K):
+        raise ValueError("A must be row-major (K-contiguous rows)")
+    lda = max(A.stride(-2), K, 1)
+    if batch > 1 and A.stride(0) != M * lda:
+        raise ValueError("batched A must have a contiguous batch stride")
+    kp, mp = sparse24_kp(K, dt), sparse24_mp(M)
+    Ac = torch.empty((batch, mp, kp // 2), dtype=torch.int8 if dt == GEMM_I8 else torch.int16,
+                     device=A.device)
+    meta = torch.empty((batch, mp, kp // 16), dtype=torch.int16, device=A.device)
+    with torch.cuda.device(A.device):
+        h = handle if handle is not None else default_handle()
+        rc = h.prune24(A.data_ptr(), M, K, lda, dt, batch, Ac.data_ptr(), meta.data_ptr(),
+                       torch.cuda.current_stream(A.device).cuda_stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_prune24")
+    return Sparse24(Ac, meta, M, K, dt, batch)
+
+
+def gemm_sparse24(sp: Sparse24, B, C=None, out=None, handle: Handle | None = None):
+    """D = prune(A) @ B + C from a Sparse24 on the current stream.  B: ((batch,) K, N)
+    of A's type, row-major or a transposed (column-major) view; C: ((batch,) M, N)
+    row-major float32 (16-bit inputs) or int32 (int8), or None for a zero C.  D is a
+    new tensor with C's strides unless ``out`` is given (``out`` may be C)."""
+    import torch
+    want = {GEMM_F16: torch.float16, GEMM_BF16: torch.bfloat16, GEMM_I8: torch.int8}[sp.dtype]
+    if B.dtype != want:
+        raise TypeError("B must have the compressed A's type")
+    if not B.is_cuda or B.device != sp.Ac.device or B.dim() not in (2, 3):
+        raise ValueError("B must be a 2-D or 3-D tensor on A's GPU")
+    M, K, N, batch = sp.M, sp.K, B.shape[-1], sp.batch
+    if B.shape[-2] != K or (B.dim() == 3 and B.shape[0] != batch) or (B.dim() == 2 and batch > 1):
+        raise ValueError("B must be (batch, K, N) with the compressed A's K and batch")
+    acc = torch.int32 if sp.dtype == GEMM_I8 else torch.float32
+    b_col, ldb = _operand_layout(B, K, N, "B")
+    shape = (batch, M, N) if B.dim() == 3 else (M, N)
+    if C is None:
+        C = torch.zeros(shape, dtype=acc, device=B.device)
+    if C.dtype != acc or tuple(C.shape) != shape or C.device != B.device:
+        raise ValueError(f"C must be {acc} of shape {shape} on B's GPU")
+    if C.stride(-1) != 1 or (M > 1 and C.stride(-2) < N):
+        raise ValueError("C must be row-major with a row stride of at least N")
+    ldc = max(C.stride(-2), N, 1)
+    if out is None:
+        out = torch.empty_strided(shape, C.stride(), dtype=acc, device=B.device)
+    if out.dtype != acc or tuple(out.shape) != shape or out.stride() != C.stride():
+        raise ValueError("out must match C's dtype, shape and strides")
+    if batch > 1 and (B.stride(0) != (N if b_col else K) * ldb or C.stride(0) != M * ldc):
+        raise ValueError("batched operands must have contiguous batch strides")
+    with torch.cuda.device(B.device):
+        h = handle if handle is not None else default_handle()
+        rc = h.run_sparse24(sp.Ac.data_ptr(), sp.meta.data_ptr(), B.data_ptr(), C.data_ptr(),
+                            out.data_ptr(), M, N, K, ldb, ldc, sp.dtype,
+                            GEMM_B_COLMAJOR if b_col else 0, batch,
+                            torch.cuda.current_stream(B.device).cuda_stream)
+    if rc != GEMM_OK:
+        raise GemmError(rc, "gemm_run_sparse24")
+    return out

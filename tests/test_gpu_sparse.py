@@ -267,3 +267,40 @@ def test_k_zero_alias_and_invalid(handle):
         assert rc == 1, kw
     torch.cuda.synchronize()
     assert torch.all(D == 3.0)
+
+
+def test_torch_front_end_sparse(handle):
+    """dmp.prune24 / dmp.gemm_sparse24 on tensors: 2-D bf16 with row-major and
+    column-major B, a batched int8 product, a zero C, and rejected arguments."""
+    import dense_mixed_precision_02_amd as dmp
+    for dt, M, N, K, batch, b_col in [("bf16", 300, 256, 520, 1, False), ("bf16", 300, 256, 520, 1, True),
+                                      ("i8", 130, 96, 384, 3, True), ("f16", 64, 64, 64, 2, False)]:
+        kw = dict(c_range=(-(1 << 20), 1 << 20)) if dt == "i8" else {}
+        p = synth.make_problem(dt, M, N, K, batch=batch, b_col=b_col, seed=610, **kw)
+        log(f"[sparse torch] {dt} {batch} x {M}x{N}x{K} b_col={b_col}")
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}[dt]
+        A = dev16(p.A).view(tdt)
+        Bs = dev16(p.B).view(tdt)                     # (batch, K, N) or (batch, N, K)
+        B = Bs.transpose(-1, -2) if b_col else Bs
+        C = torch.from_numpy(p.C).cuda()
+        if batch == 1:
+            A, B, C = A[0], B[0], C[0]
+        sp = dmp.prune24(A)
+        D = dmp.gemm_sparse24(sp, B, C)
+        torch.cuda.synchronize()
+        pruned = oracle.prune24(dt, p.A, p.M, p.K, p.lda, p.batch)
+        check(p, pruned, D.cpu().numpy().reshape(p.batch, p.M, p.ldc))
+        # zero C
+        D0 = dmp.gemm_sparse24(sp, B)
+        torch.cuda.synchronize()
+        z = synth.Problem(dt, M, N, K, batch, p.lda, p.ldb, p.ldc, False, b_col, p.A, p.B,
+                          np.zeros_like(p.C))
+        check(z, pruned, D0.cpu().numpy().reshape(p.batch, p.M, p.ldc))
+    A = torch.zeros((64, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        dmp.prune24(A)
+    sp = dmp.prune24(torch.zeros((64, 64), dtype=torch.float16, device="cuda"))
+    with pytest.raises(TypeError):
+        dmp.gemm_sparse24(sp, torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        dmp.gemm_sparse24(sp, torch.zeros((32, 64), dtype=torch.float16, device="cuda"))
