@@ -143,7 +143,6 @@ class Handle:
             raise GemmError(rc, "gemm_run_ex")
 
 
-_default = {}
 
 
 def sparse24_kp(K: int, dtype: int = GEMM_F16) -> int:
@@ -158,13 +157,23 @@ def sparse24_mp(M: int) -> int:
     return -(-M // 16) * 16
 
 
+_tls = threading.local()
+
+
 def default_handle() -> Handle:
+    """The handle the torch front ends use: one per host thread, device and
+    stream, since a handle's workspace must not serve two calls that can run at
+    the same time (one thread at a time, one stream at a time)."""
     import torch
     dev = torch.cuda.current_device()
-    h = _default.get(dev)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    handles = getattr(_tls, "handles", None)
+    if handles is None:
+        handles = _tls.handles = {}
+    h = handles.get(key)
     if h is None:
         h = Handle()
-        _default[dev] = h
+        handles[key] = h
     return h
 
 

@@ -266,3 +266,29 @@ def test_int8_transposed_b_path(handle):
         log(f"[i8-bT] {batch} x {M}x{N}x{K} pad={pad} {lbl}")
         assert "row->col" in lbl
         check_full(p, gpu_result(handle, p))
+
+
+def test_front_end_streams_get_their_own_workspace(handle):
+    """Two split-K products issued on two streams without synchronising in between:
+    the front end's default handle differs per stream (each has its own workspace),
+    so both results are right."""
+    import dense_mixed_precision_02_amd as dmp
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    probs = [synth.make_problem("bf16", 256, 256, 8192, seed=s, b_col=True) for s in (71, 72)]
+    outs = []
+    with torch.cuda.stream(s1):
+        h1 = dmp.default_handle()
+    with torch.cuda.stream(s2):
+        h2 = dmp.default_handle()
+    assert h1 is not h2 and h1.ptr.value != h2.ptr.value
+    torch.cuda.synchronize()
+    for p, st in zip(probs, (s1, s2)):
+        A, B, C = to_device(p)
+        with torch.cuda.stream(st):
+            At = A.view(torch.bfloat16)[0]
+            Bt = B.view(torch.bfloat16)[0].t()        # column-major view
+            outs.append(dmp.gemm(At, Bt, C[0]))
+    torch.cuda.synchronize()
+    for p, D in zip(probs, outs):
+        log(f"[streams] bf16 {p.M}x{p.N}x{p.K} {dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, 1, 2)}")
+        check_full(p, D.cpu().numpy().reshape(1, p.M, p.ldc))
