@@ -72,6 +72,25 @@ def test_golden_tables_match_the_printed_formulas():
         assert len(set(m.values())) == len(m), shape
 
 
+def converse(shape, lane, g):
+    """The page's converse formulas: (block, row, col) held in lane L, register G."""
+    if shape == "32x32":
+        return g // 16, (8 * (g // 4)) % 32 + 4 * (lane // 32) + g % 4, lane % 32
+    if shape == "16x16":
+        return g // 4, 4 * (lane // 16) + g % 4, lane % 16
+    if shape == "4x4":
+        return lane // 4, g % 4, lane % 4
+    if shape == "16x16f64":
+        return 0, 4 * g + lane // 16, lane % 16
+    raise KeyError(shape)
+
+
+def test_golden_tables_match_the_printed_converse_formulas():
+    for shape, m in load_golden().items():
+        for (b, i, j), (lane, g) in m.items():
+            assert converse(shape, lane, g) == (b, i, j), (shape, b, i, j, lane, g)
+
+
 # probe id, table shape, k summed per output element
 PROBES = [
     (0, "32x32", 16, "mfma_f32_32x32x16_f16"),
