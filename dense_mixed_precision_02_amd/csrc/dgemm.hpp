@@ -37,9 +37,12 @@ struct DgemmArgs {
 //     granule g (k = 2g, 2g+1) sits in slot g ^ swz(r), so that the 16 rows a
 //     fragment read touches spread over all banks.
 //   MN-contiguous operand: k-row k occupies bytes [8 R k, 8 R (k+1)); granule p
-//     (rows 2p, 2p+1) sits in slot p ^ 8*((k>>1)&1), which moves every other pair
-//     of k-rows by 128 bytes so that the four k-rows one read touches alternate
-//     between the two halves of the banks.
+//     (rows 2p, 2p+1) sits in slot p, unswizzled.  A swizzle that moved every
+//     other pair of k-rows by 128 bytes (so that the four k-rows one read touches
+//     alternate between the halves of a 256-byte bank window) made the 4096^3
+//     launch with a row-major B 7 % slower (2138 against 1981 us, timed
+//     interleaved); dropping the K-contiguous operand's swizzle as well made it
+//     slower again (2095 us).
 template <int R, bool KCONTIG>
 struct Op64 {
     static constexpr int BYTES = R * 128;
@@ -52,7 +55,6 @@ struct Op64 {
     int kk[CPW];   // k index of the granule's first element within the tile
 
     __device__ static int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-    __device__ static int kswz(int k) { return 8 * ((k >> 1) & 1); }
 
     __device__ void init(int wave, int lane, int64_t ld) {
 #pragma unroll
@@ -67,7 +69,7 @@ struct Op64 {
             } else {
                 const int q = c * 64 + lane;          // granule index in k-row-major order
                 const int k = q / (R / 2);
-                const int p = (q % (R / 2)) ^ kswz(k);
+                const int p = q % (R / 2);
                 rr[j] = 2 * p;
                 kk[j] = k;
                 off[j] = (int)(k * ld + 2 * p) * 8;
@@ -101,8 +103,8 @@ struct Op64 {
             const int k0 = 8 * d + 2 * q;
             doublex2 v;
             const int p = row >> 1, h = (row & 1) * 8;
-            v.x = *(const DMP_LDS double *)(lds + k0 * (R * 8) + ((p ^ kswz(k0)) << 4) + h);
-            v.y = *(const DMP_LDS double *)(lds + (k0 + 1) * (R * 8) + ((p ^ kswz(k0 + 1)) << 4) + h);
+            v.x = *(const DMP_LDS double *)(lds + k0 * (R * 8) + (p << 4) + h);
+            v.y = *(const DMP_LDS double *)(lds + (k0 + 1) * (R * 8) + (p << 4) + h);
             return v;
         }
     }
