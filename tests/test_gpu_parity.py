@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (DTYPE_CODE, check_full, check_points, check_row_sums, log, run, sample_points,
+from gpu_util import (DTYPE_CODE, check_full, check_points, check_row_sums, log, logical_D, run, sample_points,
                       to_device)
 
 torch = pytest.importorskip("torch")
@@ -292,3 +292,32 @@ def test_front_end_streams_get_their_own_workspace(handle):
     for p, D in zip(probs, outs):
         log(f"[streams] bf16 {p.M}x{p.N}x{p.K} {dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, 1, 2)}")
         check_full(p, D.cpu().numpy().reshape(1, p.M, p.ldc))
+
+
+@pytest.mark.parametrize("case", ["f16-subnormal-inputs", "bf16-subnormal-inputs",
+                                  "bf16-subnormal-results"])
+def test_subnormals_are_kept(handle, case):
+    """Subnormal fp16/bf16 inputs and fp32-subnormal products are not flushed to
+    zero: with C = 0 every output is a sum of tiny products that a flush would
+    lose entirely, so the result must be non-zero and within the bound (whose
+    S-term is itself tiny) on the tile and element-wise kernels."""
+    dt = case.split("-")[0]
+    for (M, N, K, b_col) in [(64, 64, 64, False), (256, 256, 256, True), (37, 41, 29, False)]:
+        p = synth.make_problem(dt, M, N, K, b_col=b_col, seed=5)
+        rng = np.random.default_rng(6)
+        sign = rng.choice([-1, 1], size=p.A.shape)
+        if case == "f16-subnormal-inputs":      # m * 2^-24: fp16 subnormals
+            p.A[...] = synth.f64_to_f16_bits(rng.integers(1, 1024, size=p.A.shape) * 2.0 ** -24 * sign)
+        else:                                  # m * 2^-133: bf16 subnormals
+            a = rng.integers(1, 128, size=p.A.shape) * 2.0 ** -133 * sign
+            p.A[...] = synth.f32_to_bf16_bits(a.astype(np.float32))
+        if case == "bf16-subnormal-results":   # products near 2^-140: fp32 subnormals
+            b = rng.integers(1, 128, size=p.B.shape) * 2.0 ** -16
+            p.B[...] = synth.f32_to_bf16_bits(b.astype(np.float32))
+        p.C[...] = 0
+        log(f"[subnormal] {case} {M}x{N}x{K} b_col={b_col}")
+        D = run(handle, p)
+        torch.cuda.synchronize()
+        Dg = logical_D(p, D.cpu().numpy())
+        assert np.all(Dg != 0), "subnormal terms were flushed"
+        check_full(p, D.cpu().numpy())
