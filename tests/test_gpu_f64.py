@@ -281,3 +281,19 @@ def test_rne_shapes_reach_every_fp64_path():
     seen = {dmp.plan_label(M, K, K, K, K, K, F64, 0).split()[0] for M, K in
             [(256, 256), (2048, 2048), (37, 37)]}
     assert seen == {"dtile64x64", "dtile128x128", "dgeneric16x16"}, seen
+
+
+def test_subnormal_inputs_are_kept(handle):
+    """fp64 subnormal A (m * 2^-1060) times ordinary B with C = 0: a flush would
+    return zeros; the results must be non-zero and within the fp64 bound on the
+    tile and element-wise kernels."""
+    for (M, N, K) in [(128, 128, 64), (37, 37, 37)]:
+        p = synth.make_problem("f64", M, N, K, seed=81)
+        rng = np.random.default_rng(82)
+        p.A[...] = np.ldexp(rng.integers(1, 1 << 20, size=p.A.shape).astype(np.float64), -1060) \
+            * rng.choice([-1.0, 1.0], size=p.A.shape)
+        p.C[...] = 0
+        log(f"[f64-subnormal] {M}x{N}x{K}")
+        D = run(handle, p)
+        assert np.all(logical(p, D.cpu().numpy()) != 0), "subnormal terms were flushed"
+        check_full(p, D)

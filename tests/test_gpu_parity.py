@@ -300,10 +300,11 @@ def test_subnormals_are_kept(handle, case):
     """Subnormal fp16/bf16 inputs and fp32-subnormal products are not flushed to
     zero: with C = 0 every output is a sum of tiny products that a flush would
     lose entirely, so the result must be non-zero and within the bound (whose
-    S-term is itself tiny) on the tile and element-wise kernels."""
+    S-term is itself tiny) on the tile, element-wise and tiny-batch kernels."""
     dt = case.split("-")[0]
-    for (M, N, K, b_col) in [(64, 64, 64, False), (256, 256, 256, True), (37, 41, 29, False)]:
-        p = synth.make_problem(dt, M, N, K, b_col=b_col, seed=5)
+    for (M, N, K, b_col, batch) in [(64, 64, 64, False, 1), (256, 256, 256, True, 1),
+                                    (37, 41, 29, False, 1), (4, 4, 16, False, 50)]:
+        p = synth.make_problem(dt, M, N, K, b_col=b_col, batch=batch, seed=5)
         rng = np.random.default_rng(6)
         sign = rng.choice([-1, 1], size=p.A.shape)
         if case == "f16-subnormal-inputs":      # m * 2^-24: fp16 subnormals
@@ -315,7 +316,7 @@ def test_subnormals_are_kept(handle, case):
             b = rng.integers(1, 128, size=p.B.shape) * 2.0 ** -16
             p.B[...] = synth.f32_to_bf16_bits(b.astype(np.float32))
         p.C[...] = 0
-        log(f"[subnormal] {case} {M}x{N}x{K} b_col={b_col}")
+        log(f"[subnormal] {case} {batch} x {M}x{N}x{K} b_col={b_col}")
         D = run(handle, p)
         torch.cuda.synchronize()
         Dg = logical_D(p, D.cpu().numpy())
