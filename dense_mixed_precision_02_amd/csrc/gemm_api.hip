@@ -62,6 +62,13 @@ hipError_t launch_f64(const Plan &P, const void *A, const void *B, const void *C
 
 template <class DT, int BM, int BN, bool AK, bool BKC>
 hipError_t launch_tile(const TileArgs &a, int64_t grid, hipStream_t s) {
+    if constexpr (BM == 64 && BN == 64) {
+        if (a.k_chunk <= 128 / DT::ESZ) {  // one k-tile per split
+            hipLaunchKernelGGL((tile_gemm<DT, BM, BN, 2, 2, AK, BKC, true>), dim3((unsigned)grid),
+                               dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((tile_gemm<DT, BM, BN, 2, 2, AK, BKC>), dim3((unsigned)grid), dim3(256), 0, s,
                        a);
     return hipGetLastError();
@@ -228,10 +235,12 @@ int gemm_plan(gemm_handle_t h, int64_t M, int64_t N, int64_t K, int64_t lda, int
         std::snprintf(label, label_len, "copy_c k=0");
         return GEMM_OK;
     }
-    std::snprintf(label, label_len, "%s %s a:%s b:%s splitk=%d grid=%lld", cfg_name(P.cfg),
+    // the 64x64 tile with one k-tile per split runs its single-buffer variant
+    const bool one = P.cfg == CFG_S && P.k_chunk <= 128 / elem_size(dtype);
+    std::snprintf(label, label_len, "%s %s a:%s b:%s splitk=%d grid=%lld%s", cfg_name(P.cfg),
                   dtype_name(dtype), (flags & GEMM_A_COLMAJOR) ? "col" : "row",
                   P.transpose_b ? "row->col" : (flags & GEMM_B_COLMAJOR) ? "col" : "row", P.splits,
-                  (long long)P.grid);
+                  (long long)P.grid, one ? " one-ktile" : "");
     return GEMM_OK;
 }
 

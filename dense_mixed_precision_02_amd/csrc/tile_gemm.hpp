@@ -178,7 +178,10 @@ __device__ static inline void interleave() {
 
 // The two LDS buffers are distinct arrays so that the compiler can tell that
 // copies into one never alias fragment reads from the other.
-template <class DT, int BM, int BN, int WM, int WN, bool AK, bool BKC>
+// ONE: every split holds at most one k-tile (K of a 64x64 batch entry, say).
+// Then a single operand buffer suffices and the epilogue's slabs reuse it, so
+// the workgroup needs 20 KB of LDS instead of 32 and more of them fit a CU.
+template <class DT, int BM, int BN, int WM, int WN, bool AK, bool BKC, bool ONE = false>
 __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -190,7 +193,10 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     using acc_t = typename DT::acc;
     using accv = typename DT::accv;
 
-    __shared__ __attribute__((aligned(1024))) char lds_a0[OpA::BYTES];
+    constexpr int SLAB_BYTES = 32 * (WTN + 8) * (int)sizeof(acc_t);   // one wave's epilogue slab
+    constexpr int ONE_BYTES = OpA::BYTES + OpB::BYTES > NW * SLAB_BYTES ? OpA::BYTES + OpB::BYTES
+                                                                        : NW * SLAB_BYTES;
+    __shared__ __attribute__((aligned(1024))) char lds_a0[ONE ? ONE_BYTES : OpA::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_b0[OpB::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_a1[OpA::BYTES];
     __shared__ __attribute__((aligned(1024))) char lds_b1[OpB::BYTES];
@@ -287,8 +293,16 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     constexpr int NMF = TM * TN;                                   // MFMAs per step
     constexpr int NRD = TM * OpA::READS + TN * OpB::READS;        // LDS reads per step
 
-    DMP_LDS char *LA[2] = {(DMP_LDS char *)lds_a0, (DMP_LDS char *)lds_a1};
-    DMP_LDS char *LB[2] = {(DMP_LDS char *)lds_b0, (DMP_LDS char *)lds_b1};
+    DMP_LDS char *LA[2], *LB[2];
+    if constexpr (ONE) {
+        LA[0] = LA[1] = (DMP_LDS char *)lds_a0;
+        LB[0] = LB[1] = (DMP_LDS char *)lds_a0 + OpA::BYTES;
+    } else {
+        LA[0] = (DMP_LDS char *)lds_a0;
+        LA[1] = (DMP_LDS char *)lds_a1;
+        LB[0] = (DMP_LDS char *)lds_b0;
+        LB[1] = (DMP_LDS char *)lds_b1;
+    }
 
     // Software pipeline.  Fragments of step s+1 are read while the MFMAs of step
     // s run.  Before the last step of k-tile kt every wave waits for k-tile kt+1
@@ -330,7 +344,19 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
         __builtin_amdgcn_sched_barrier(0);
         step_sync();
     };
-    if (nkt > 0) {
+    if constexpr (ONE) {
+        // nkt is 0 or 1; a single k-tile is k-tile 1 of the padded count
+        if (nkt > 0) {
+            stage_part(1, LA[0], LB[0], Z{}, I2{});
+            wait_vmcnt<0>();
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                read(fa0, fb0, LA[0], LB[0], s);
+                mma(fa0, fb0);
+            }
+        }
+    } else if (nkt > 0) {
         stage_part(0, LA[0], LB[0], Z{}, I2{});
         wait_vmcnt<0>();
         __syncthreads();
@@ -351,7 +377,8 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     // as 16-byte vectors covering whole row segments.
     wait_vmcnt<0>();  // the zero-fill loads issued past the last k-tile have landed
     __syncthreads();  // every wave is done with the operand buffers
-    DMP_LDS char *slab_c = wave == 0 ? LA[0] : wave == 1 ? LB[0] : wave == 2 ? LA[1] : LB[1];
+    DMP_LDS char *slab_c = ONE ? (DMP_LDS char *)lds_a0 + wave * SLAB_BYTES
+                         : wave == 0 ? LA[0] : wave == 1 ? LB[0] : wave == 2 ? LA[1] : LB[1];
     DMP_LDS acc_t *slab = (DMP_LDS acc_t *)slab_c;
     constexpr int SP = WTN + 8;        // padded slab row (elements): rows r and r+4 land 128 B apart mod 256
     static_assert(32 * SP * 4 <= OpA::BYTES && 32 * SP * 4 <= OpB::BYTES, "slab must fit");

@@ -106,11 +106,23 @@ def test_plans_of_the_workloads():
     # skinny 1024 x 1024 x 65536: 16 tiles x 16 K-splits
     assert dmp.plan_label(1024, 1024, 65536, 65536, 1024, 1024, dmp.GEMM_BF16) == \
         "tile256x256 bf16 a:row b:row splitk=16 grid=256"
-    # 8192 batched 64^3
+    # 8192 batched 64^3: one k-tile, so the single-buffer variant of the 64x64 tile
     assert dmp.plan_label(64, 64, 64, 64, 64, 64, dmp.GEMM_F16, 0, 8192) == \
-        "tile64x64 f16 a:row b:row splitk=1 grid=8192"
-    # 256^3 fp16
-    assert dmp.plan_label(256, 256, 256, 256, 256, 256, dmp.GEMM_F16).startswith("tile64x64")
+        "tile64x64 f16 a:row b:row splitk=1 grid=8192 one-ktile"
+    # 256^3 fp16: four k-tiles, the pipelined kernel
+    assert dmp.plan_label(256, 256, 256, 256, 256, 256, dmp.GEMM_F16) == \
+        "tile64x64 f16 a:row b:row splitk=1 grid=16"
+
+
+def test_single_buffer_variant_only_for_one_ktile():
+    """The k-tile is 128 bytes of K: 64 fp16/bf16 elements, 128 int8 ones."""
+    f16 = lambda K, b=1: dmp.plan_label(64, 64, K, K, 64, 64, dmp.GEMM_F16, 0, b)
+    i8 = lambda K: dmp.plan_label(64, 64, K, K, 64, 64, dmp.GEMM_I8, 0, 1)
+    assert f16(64).endswith("one-ktile") and f16(16).endswith("one-ktile")
+    assert not f16(72).endswith("one-ktile") and not f16(128).endswith("one-ktile")
+    assert i8(128).endswith("one-ktile") and not i8(144).endswith("one-ktile")
+    # other tiles never use it
+    assert not dmp.plan_label(4096, 4096, 64, 64, 4096, 4096, dmp.GEMM_F16).endswith("one-ktile")
 
 
 def test_generic_path_when_granules_do_not_fit():

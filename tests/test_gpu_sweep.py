@@ -98,7 +98,8 @@ def test_random_sweep_against_the_oracle(handle, chunk):
         flags = (1 if a_col else 0) | (2 if b_col else 0) | \
                 (A_SHARED if "A" in shared else 0) | (B_SHARED if "B" in shared else 0)
         label = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, CODE[dt], flags, batch)
-        paths.add(label.split()[0] + (" split" if "splitk=1 " not in label + " " else ""))
+        paths.add(label.split()[0] + (" split" if "splitk=1 " not in label + " " else "") +
+                  (" one-ktile" if label.endswith("one-ktile") else ""))
         log(f"[sweep {n}] {dt} {batch} x {M}x{N}x{K} a_col={a_col} b_col={b_col} pad={pad} "
             f"shared={shared or '-'} ex={ex} {label}")
         A, B = dev(p.A), dev(p.B)
@@ -153,7 +154,7 @@ def test_sweep_reached_every_path():
     if len(PATHS) == 0:
         pytest.skip("the sweep did not run")
     log(f"[sweep] paths reached: {sorted(PATHS)}")
-    for need in ("tile64x64", "tile128x128", "tile256x256", "generic32x32", "tiny4x4x16b",
+    for need in ("tile64x64", "tile64x64 one-ktile", "tile128x128", "tile256x256", "generic32x32", "tiny4x4x16b",
                  "tiny16x16x4b", "dtile64x64", "dgeneric16x16", "copy",
                  "tile256x256 split", "tile64x64 split"):
         assert any(x.startswith(need) for x in PATHS), (need, sorted(PATHS))
