@@ -164,7 +164,7 @@ hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, c
     const int acc_ty = acc_type(dtype);
     t.flat_out = ldc == N && ep.d_type == acc_ty && (!ep.use_c || ep.c_type == acc_ty) &&
                  (uintptr_t)D % 16 == 0 && (!ep.use_c || (uintptr_t)C % 16 == 0) &&
-                 (sC * 4) % 16 == 0 && nb * sC * 4 <= TINY_OUT;
+                 (sC * 4) % 16 == 0 && nb * sC * 4 <= tiny_out_bytes(P.cfg == CFG_TINY4 ? 4 : 16);
     t.ep = ep;
     if (dtype == GEMM_F16) return launch_tiny_dt<F16>(P.cfg, t, sa, sb, P.grid, s);
     if (dtype == GEMM_BF16) return launch_tiny_dt<BF16>(P.cfg, t, sa, sb, P.grid, s);

@@ -36,9 +36,11 @@ struct TinyArgs {
     EpiParams ep;
 };
 
-// LDS bytes per wave: one operand region each for A and B, and the output region.
+// LDS bytes per wave: one operand region each for A and B, and the output region,
+// sized for the dense outputs of the wave's problems (16 of at most 4x4 with the
+// 4x4 blocks, 4 of at most 16x16 with the 16x16 ones).
 constexpr int TINY_STAGE = 2048;
-constexpr int TINY_OUT = 4096;
+constexpr int tiny_out_bytes(int S) { return S == 4 ? 16 * 4 * 4 * 4 : 4 * 16 * 16 * 4; }
 
 // Instruction for S x S blocks of element type DT (4 k per instruction).
 template <class DT, int S> struct Multi;
@@ -165,6 +167,7 @@ __global__ __launch_bounds__(256) void tiny_gemm(const TinyArgs p) {
     constexpr int BG = SB ? 4 : 0;                    // lanes 0-15's B to all lane groups
     using I = Multi<DT, S>;
     using acc_t = typename DT::acc;
+    constexpr int TINY_OUT = tiny_out_bytes(S);
     __shared__ __attribute__((aligned(16))) char lds[4 * (2 * TINY_STAGE + TINY_OUT)];
     const int lane = lane_id(), wave = wave_id();
     const int64_t base = ((int64_t)blockIdx.x * 4 + wave) * NB;
