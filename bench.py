@@ -186,6 +186,145 @@ def parity_sample(p, D_host, ex=None, sparse=False):
     return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
 
 
+CEIL_LIB = os.path.join(ROOT, "tests", "native", "libceiling_probe.so")
+# matrix-instruction probes of tests/native/ceiling_probe.hip: (id, name, dtype, work per CU-clock
+# at the datasheet rate, for the fraction of the published peak)
+CEIL_MFMA = [(0, "mfma_f32_32x32x16_bf16", "bf16"), (1, "mfma_f32_32x32x16_f16", "f16"),
+             (2, "mfma_f32_16x16x32_bf16", "bf16"), (3, "mfma_f32_16x16x32_f16", "f16"),
+             (4, "mfma_i32_32x32x32_i8", "i8"), (5, "mfma_i32_16x16x64_i8", "i8"),
+             (6, "mfma_f64_16x16x4_f64", "f64"), (7, "smfmac_f32_32x32x32_bf16", "sp_bf16"),
+             (8, "smfmac_i32_32x32x64_i8", "sp_i8")]
+CEIL_PEAK = {"bf16": 2516.6, "f16": 2516.6, "i8": 5033.2, "f64": 78.6, "sp_bf16": 5033.2,
+             "sp_i8": 10066.4}
+
+
+def ceiling_probes(quick: bool = False, target_ms: float = 20.0, launches: int = 8):
+    """Sustained ceilings of this part, measured by the test-side probe library:
+    each matrix instruction alone (one workgroup of four waves per CU, plus two per
+    CU for bf16 32x32x16), L2-resident loads into registers and straight into LDS,
+    LDS reads, and HBM streams.  Returns a list of dicts (one per probe); each
+    launch is timed with HIP events on the launch stream, the first launch of
+    each probe calibrates its length to about target_ms and is not counted."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    if not os.path.exists(CEIL_LIB):
+        raise RuntimeError(f"{CEIL_LIB} is not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(CEIL_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_longlong
+    lib.ceil_ops_per_inst.restype = i64
+    lib.ceil_ops_per_inst.argtypes = [ctypes.c_int]
+    lib.ceil_insts_per_trip.argtypes = [ctypes.c_int]
+    lib.ceil_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.ceil_read.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, ctypes.c_int, vp, vp]
+    lib.ceil_lds.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.ceil_hbm.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, vp]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    if quick:
+        target_ms, launches = 2.0, 3
+
+    def timed(launch, n):
+        ts = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert launch() == 0
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return ts
+
+    out = []
+    rng = np.random.default_rng(77)
+    bits = torch.from_numpy(rng.integers(-2**31, 2**31, size=256 * 4, dtype=np.int64)
+                            .astype(np.int32)).to(dev)
+    # bf16 / fp16 operand bits: keep exponents moderate so the sums stay finite
+    bits16 = torch.from_numpy((rng.integers(0, 2**16, size=256 * 8) & 0x3FFF | 0x3000)
+                              .astype(np.uint16).view(np.int16)).to(dev)
+    for which, name, dt in CEIL_MFMA:
+        for per_cu in ((1, 2) if which == 0 else (1,)):
+            grid = cus * per_cu
+            sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+            clk = torch.zeros(grid * 4 * 4, dtype=torch.int64, device=dev)
+            src = bits16 if dt in ("bf16", "f16", "sp_bf16") else bits
+            iters = 2000
+            t = timed(lambda: lib.ceil_mfma(which, grid, iters, src.data_ptr(), sink.data_ptr(),
+                                            clk.data_ptr(), sp), 1)[0]
+            iters = max(100, int(iters * (target_ms * 1e-3) / max(t, 1e-6)))
+            ts = timed(lambda: lib.ceil_mfma(which, grid, iters, src.data_ptr(), sink.data_ptr(),
+                                             clk.data_ptr(), sp), launches)
+            c = clk.view(grid * 4, 4).cpu().numpy().astype(np.float64)
+            ops = float(lib.ceil_ops_per_inst(which)) * lib.ceil_insts_per_trip(which) * iters \
+                * grid * 4
+            rates = [ops / x / 1e12 for x in ts]
+            med = float(np.median(ts))
+            # shader-clock counter ticks per second over the last launch
+            clock = float(np.mean(c[:, 1] - c[:, 0])) / ts[-1] / 1e9
+            rt = float(np.mean(c[:, 3] - c[:, 2])) / ts[-1] / 1e6
+            out.append({"probe": name, "waves_per_simd": per_cu, "grid": grid, "iters": iters,
+                        "launch_ms": round(med * 1e3, 3),
+                        "rate": round(ops / med / 1e12, 1),
+                        "unit": "TOP/s" if "i8" in dt else "TFLOP/s",
+                        "first_last": [round(rates[0], 1), round(rates[-1], 1)],
+                        "frac_of_datasheet": round(ops / med / 1e12 / CEIL_PEAK[dt], 4),
+                        "clock_counter_ghz": round(clock, 3), "realtime_counter_mhz": round(rt, 2)})
+            print(f"[ceiling] {out[-1]}", file=sys.stderr, flush=True)
+    # loads from an L2-resident buffer (1 MB, every workgroup sweeps all of it)
+    l2 = torch.zeros(1 << 20, dtype=torch.uint8, device=dev)
+    for kind, what in ((0, "l2_read_to_registers"), (1, "l2_read_direct_to_lds")):
+        for per_cu in (1, 2):
+            grid = cus * per_cu
+            sink = torch.empty(grid * 256 * 4, dtype=torch.int32, device=dev)
+            passes = 4
+            t = timed(lambda: lib.ceil_read(kind, grid, l2.data_ptr(), l2.numel(), passes,
+                                            sink.data_ptr(), sp), 1)[0]
+            passes = max(1, int(passes * (target_ms * 1e-3) / max(t, 1e-6)))
+            ts = timed(lambda: lib.ceil_read(kind, grid, l2.data_ptr(), l2.numel(), passes,
+                                             sink.data_ptr(), sp), launches)
+            med = float(np.median(ts))
+            nbytes = float(grid) * passes * l2.numel()
+            out.append({"probe": what, "workgroups_per_cu": per_cu, "grid": grid,
+                        "buffer_bytes": l2.numel(), "passes": passes,
+                        "launch_ms": round(med * 1e3, 3), "rate": round(nbytes / med / 1e12, 2),
+                        "unit": "TB/s"})
+            print(f"[ceiling] {out[-1]}", file=sys.stderr, flush=True)
+    # LDS reads
+    grid = cus
+    sink = torch.empty(grid * 256 * 4, dtype=torch.int32, device=dev)
+    iters = 1000
+    t = timed(lambda: lib.ceil_lds(grid, iters, sink.data_ptr(), sp), 1)[0]
+    iters = max(10, int(iters * (target_ms * 1e-3) / max(t, 1e-6)))
+    ts = timed(lambda: lib.ceil_lds(grid, iters, sink.data_ptr(), sp), launches)
+    med = float(np.median(ts))
+    nbytes = float(grid) * 256 * 16 * 16 * iters
+    out.append({"probe": "lds_read_b128", "grid": grid, "iters": iters,
+                "launch_ms": round(med * 1e3, 3), "rate": round(nbytes / med / 1e12, 2),
+                "unit": "TB/s", "bytes_per_cu_per_ns": round(nbytes / med / 1e9 / cus, 1)})
+    print(f"[ceiling] {out[-1]}", file=sys.stderr, flush=True)
+    # HBM streams over 2 GiB (far beyond the 256 MB memory-side cache)
+    nbytes = (256 << 20) if quick else (2 << 30)
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    sink = torch.empty(256 * 4, dtype=torch.int32, device=dev)
+    n16 = nbytes // 16
+    for mode, what, moved in ((0, "hbm_read_nt", 1), (1, "hbm_write_nt", 1), (2, "hbm_copy_nt", 2)):
+        grid = cus * 8
+        ts = timed(lambda: lib.ceil_hbm(mode, grid, a.data_ptr(), b.data_ptr(), n16, sink.data_ptr(),
+                                        sp), launches + 1)[1:]
+        med = float(np.median(ts))
+        out.append({"probe": what, "bytes": nbytes, "grid": grid, "launch_ms": round(med * 1e3, 3),
+                    "rate": round(moved * nbytes / med / 1e12, 2), "unit": "TB/s"})
+        print(f"[ceiling] {out[-1]}", file=sys.stderr, flush=True)
+    del a, b
+    torch.cuda.synchronize()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +341,9 @@ def main(argv=None):
     ap.add_argument("--rotate", type=int, default=None,
                     help="device copies of the inputs and outputs the timed steps rotate over "
                          f"(default {ROTATE_SETS} for {sorted(ROTATE)}, else 1)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only run the ceiling probes (matrix-instruction rates, L2 / LDS / HBM "
+                         "bandwidth) and print one JSON line per probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of COPY_BYTES (counter calibration)")
     args = ap.parse_args(argv)
@@ -213,6 +355,11 @@ def main(argv=None):
 
     import numpy as np
     import torch
+
+    if args.ceiling:
+        for r in ceiling_probes():
+            print(json.dumps(r), flush=True)
+        return
 
     if args.copy_probe:
         x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")

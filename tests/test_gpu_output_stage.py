@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import DTYPE_CODE, log, sample_points
+from gpu_util import DTYPE_CODE, log
 
 torch = pytest.importorskip("torch")
 
@@ -194,12 +194,11 @@ def exact_check(handle, p, d_type, c_type, pts=None, in_place=False):
 @pytest.mark.parametrize("d_type", FLOAT_TYPES)
 @pytest.mark.parametrize("name", ["C1", "C4", "C5"])
 def test_exact_inputs_bit_exact(handle, name, d_type):
-    """Tile (C1 shape), batched 64x64 tiles (C4) and split-K (C5) paths."""
+    """Tile (C1 shape), batched 64x64 tiles (C4) and split-K (C5) paths, every element."""
     p = synth.exact_variant(name)
     c_type = "bf16" if d_type == "f32" else d_type
     log(f"[exact-out] {name} C:{c_type} D:{d_type}")
-    pts = sample_points(p, 400, seed=7) if name == "C5" else None
-    exact_check(handle, p, d_type, c_type, pts=pts)
+    exact_check(handle, p, d_type, c_type)
 
 
 @pytest.mark.parametrize("d_type", ["f16", "bf16"])

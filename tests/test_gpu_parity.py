@@ -7,8 +7,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (DTYPE_CODE, check_full, check_points, check_row_sums, log, logical_D, run, sample_points,
-                      to_device)
+from gpu_util import DTYPE_CODE, check_full, check_row_sums, log, logical_D, run, to_device
 
 torch = pytest.importorskip("torch")
 
@@ -33,37 +32,32 @@ def gpu_result(handle, p, **kw):
 
 # ------------------------------------------------------------------ workloads
 
-SAMPLES = {"C2": 3000, "C3": 3000, "C5": 600, "S1": 3000}
-
-
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "S1"])
 def test_workload_parity(handle, name):
+    """Every element of D at each workload's full size against the full oracle: int8
+    bit for bit, fp16/bf16 within the per-element bound.  The row sums are an
+    extra check of the same output."""
     import dense_mixed_precision_02_amd as dmp
     p = synth.config_problem(name)
     flags = (1 if p.a_col else 0) | (2 if p.b_col else 0)
     lbl = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, DTYPE_CODE[p.dtype], flags, p.batch)
     log(f"[parity] {name}: {synth.CONFIG_LABELS[name]} plan={lbl}")
     D = gpu_result(handle, p)
-    if name in ("C1", "C4"):
-        r = check_full(p, D)
-    else:
-        r = check_points(p, D, sample_points(p, SAMPLES[name], seed=sum(map(ord, name))))
+    r = check_full(p, D)
     check_row_sums(p, D)
-    log(f"[parity] {name}: ok, max err/bound {r:.3g}")
+    log(f"[parity] {name}: ok, every element, max err/bound {r:.3g}")
 
 
 @pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "S1"])
 def test_workload_exact_integer_inputs(handle, name):
     """A, B in {-1, 0, 1} and small-integer C at each workload's shape: every partial sum is
-    an integer below 2^24 in magnitude, so the result must equal the oracle exactly."""
+    an integer below 2^24 in magnitude, so every element must equal the oracle exactly."""
     p = synth.exact_variant(name)
     log(f"[exact] {name}")
     D = gpu_result(handle, p)
-    if name in ("C1", "C4"):
-        check_full(p, D, exact=True)
-    else:
-        check_points(p, D, sample_points(p, 800 if name != "C5" else 300, seed=5), exact=True)
+    check_full(p, D, exact=True)
     check_row_sums(p, D, exact=True)
+    log(f"[exact] {name}: every element identical")
 
 
 # ------------------------------------------------------------ shapes / layouts
