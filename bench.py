@@ -325,59 +325,19 @@ def ceiling_probes(quick: bool = False, target_ms: float = 20.0, launches: int =
     return out
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", default="C2")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--d-type", choices=["f32", "f16", "bf16"], default=None,
-                    help="time gemm_run_ex with this D storage type")
-    ap.add_argument("--c-type", choices=["f32", "f16", "bf16", "none"], default="f32")
-    ap.add_argument("--alpha", type=float, default=1.0)
-    ap.add_argument("--beta", type=float, default=1.0)
-    ap.add_argument("--rotate", type=int, default=None,
-                    help="device copies of the inputs and outputs the timed steps rotate over "
-                         f"(default {ROTATE_SETS} for {sorted(ROTATE)}, else 1)")
-    ap.add_argument("--ceiling", action="store_true",
-                    help="only run the ceiling probes (matrix-instruction rates, L2 / LDS / HBM "
-                         "bandwidth) and print one JSON line per probe")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run a plain device copy of COPY_BYTES (counter calibration)")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
-
+def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None):
+    """Upload workload `name`, run `warmup` untimed steps, then `reps` repetitions
+    of exactly `steps` timed steps each (HIP events on the launch stream, with a
+    device synchronisation before and after each repetition).  One step is one
+    call of the library on the whole problem.  Returns a dict with the problem,
+    the per-repetition times, the median, the plan label and the last output."""
     import numpy as np
     import torch
 
-    if args.ceiling:
-        for r in ceiling_probes():
-            print(json.dumps(r), flush=True)
-        return
-
-    if args.copy_probe:
-        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
-        y = torch.empty_like(x)
-        for _ in range(6):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 6}))
-        return
-
     import dense_mixed_precision_02_amd as dmp
     import synth
-    from bench_profile import kernel_source_hash, read_traffic
 
-    name = args.config
     p = synth.config_problem(name)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
 
     def up(x):
         t = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x)
@@ -386,14 +346,15 @@ def main(argv=None):
     ex = None
     sparse = name in SPARSE_CONFIGS
     A, B = up(p.A), up(p.B)
-    if args.d_type is not None:
+    if ex_args is not None:
+        c_type, d_type, alpha, beta_in = ex_args
         if p.dtype == "i8":
             raise SystemExit("--d-type applies to fp16/bf16 workloads")
-        beta = 0.0 if args.c_type == "none" else args.beta
-        Cst = store_c(args.c_type, p.C) if args.c_type != "none" else None
-        ex = (args.c_type, args.d_type, args.alpha, beta, Cst)
+        beta = 0.0 if c_type == "none" else beta_in
+        Cst = store_c(c_type, p.C) if c_type != "none" else None
+        ex = (c_type, d_type, alpha, beta, Cst)
         C = up(Cst) if Cst is not None else None
-        D = torch.empty(p.C.shape, dtype=torch.float32 if args.d_type == "f32" else torch.int16,
+        D = torch.empty(p.C.shape, dtype=torch.float32 if d_type == "f32" else torch.int16,
                         device=dev)
     else:
         C = up(p.C)
@@ -402,12 +363,12 @@ def main(argv=None):
     flags = (dmp.GEMM_A_COLMAJOR if p.a_col else 0) | (dmp.GEMM_B_COLMAJOR if p.b_col else 0)
     code = DTYPE_CODE[p.dtype]
     label = dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, code, flags, p.batch, handle=h)
-    if name in SPARSE_CONFIGS:
+    if sparse:
         ins = "smfmac32x32x64" if p.dtype == "i8" else "smfmac32x32x32"
         label = f"sparse24 {ins} tile256x256 grid={-(-p.M // 256) * -(-p.N // 256) * p.batch}"
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    nsets = args.rotate if args.rotate else (ROTATE_SETS if name in ROTATE else 1)
+    nsets = rotate if rotate else (ROTATE_SETS if name in ROTATE else 1)
     if sparse:
         nsets = 1  # the sparse products time one compressed A
     # set 0 is (A, B, C, D); further sets are device copies of the same inputs
@@ -451,24 +412,34 @@ def main(argv=None):
         def step(i):
             h.run_ex(*runs[i % nsets], **kw)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # events on the stream the kernels are launched on
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
-    flops = p.flops
-    tflops = flops / (ms * 1e-3) / 1e12
+    rep_ms = []
+    t_all = time.perf_counter()
+    for r in range(reps):
+        # events on the stream the kernels are launched on
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rep_ms.append(e0.elapsed_time(e1) / steps)
+    wall = time.perf_counter() - t_all
     D_host = D.cpu().numpy()
+    h.close()
+    return {"p": p, "ex": ex, "sparse": sparse, "label": label, "nsets": nsets,
+            "rep_ms": rep_ms, "ms": float(np.median(rep_ms)), "wall": wall, "D_host": D_host,
+            "prune_us": prune_us}
 
+
+def roofline_of(name, r):
+    """(throughput, unit, peak, roofline dict, algorithmic bytes) of a timed workload."""
+    p, ex, sparse, ms = r["p"], r["ex"], r["sparse"], r["ms"]
+    tflops = p.flops / (ms * 1e-3) / 1e12
     peak = SPARSE_PEAK_TFLOPS[p.dtype] if sparse else PEAK_TFLOPS[p.dtype]
     unit = "TOP/s" if p.dtype == "i8" else "TFLOP/s"
     nbytes = algorithmic_bytes(p, *(ex[:2] if ex else (None, None)), sparse=sparse)
@@ -480,10 +451,89 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": unit,
                 "frac": round(tflops / peak, 4), "traffic": None}
     # measured HBM bytes per launch, only while the kernel sources are unchanged
+    from bench_profile import kernel_source_hash, read_traffic
     tf = TRAFFIC_FILES.get(name)
     rt = read_traffic(os.path.join(ROOT, tf)) if tf and ex is None else None
     if rt is not None and rt[1] == kernel_source_hash():
         roof["traffic"] = round(rt[0])
+    return tflops, unit, peak, roof, nbytes
+
+
+# Workloads timed beside the headline one in the default run, so that every input
+# type the metric names is measured: the 4096^3 fp16 product and the 8192^3 int8 one.
+EXTRA_WORKLOADS = ("S1", "C3")
+
+
+def single_core_c1():
+    """The oracle on one host thread over the whole 256^3 fp16 workload."""
+    import oracle
+    import synth
+    p = synth.config_problem("C1")
+    oracle.gemm(p.dtype, p.A, p.B, p.C, nthreads=1, **p.oracle_args())  # loads the library
+    t = time.perf_counter()
+    oracle.gemm(p.dtype, p.A, p.B, p.C, nthreads=1, **p.oracle_args())
+    dt = time.perf_counter() - t
+    return {"value": p.flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole 256x256x256 fp16 workload ({p.flops // 2} MACs, {dt:.3f} s)"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="repetitions of the timed steps; the line reports the median")
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-extra", action="store_true",
+                    help=f"skip the workloads timed beside the default one ({', '.join(EXTRA_WORKLOADS)})")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--d-type", choices=["f32", "f16", "bf16"], default=None,
+                    help="time gemm_run_ex with this D storage type")
+    ap.add_argument("--c-type", choices=["f32", "f16", "bf16", "none"], default="f32")
+    ap.add_argument("--alpha", type=float, default=1.0)
+    ap.add_argument("--beta", type=float, default=1.0)
+    ap.add_argument("--rotate", type=int, default=None,
+                    help="device copies of the inputs and outputs the timed steps rotate over "
+                         f"(default {ROTATE_SETS} for {sorted(ROTATE)}, else 1)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only run the ceiling probes (matrix-instruction rates, L2 / LDS / HBM "
+                         "bandwidth) and print one JSON line per probe")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of COPY_BYTES (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.ceiling:
+        for r in ceiling_probes():
+            print(json.dumps(r), flush=True)
+        return
+
+    if args.copy_probe:
+        x = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(6):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": COPY_BYTES, "launches": 6}))
+        return
+
+    import synth
+
+    name = args.config
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ex_args = (args.c_type, args.d_type, args.alpha, args.beta) if args.d_type else None
+    r = time_workload(name, args.steps, args.warmup, args.reps, ex_args, args.rotate, dev)
+    p, ex, sparse, ms = r["p"], r["ex"], r["sparse"], r["ms"]
+    tflops, unit, peak, roof, nbytes = roofline_of(name, r)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -499,23 +549,42 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": synth.CONFIG_LABELS[name], "M": p.M, "N": p.N, "K": p.K,
                    "batch": p.batch, "a_layout": "col" if p.a_col else "row",
-                   "b_layout": "col" if p.b_col else "row", "plan": label,
+                   "b_layout": "col" if p.b_col else "row", "plan": r["label"],
                    "pct_of_dense_peak": round(100 * tflops / peak, 2),
                    "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                   "timed_wall_s": round(wall, 3), "input_sets": nsets},
+                   "repetitions": args.reps,
+                   "rep_ms_per_step": [round(x, 5) for x in r["rep_ms"]],
+                   "timed_wall_s": round(r["wall"], 3), "input_sets": r["nsets"]},
         "roofline": roof,
-        "parity": parity_sample(p, D_host, ex, sparse),
+        "parity": parity_sample(p, r["D_host"], ex, sparse),
     }
     if sparse:
-        line["config"]["prune_us"] = round(prune_us, 1)
+        line["config"]["prune_us"] = round(r["prune_us"], 1)
         line["config"]["note"] = ("value = 2*M*N*K / time, the dense-equivalent rate of the 2:4 "
                                   "product; peak = the sparse instructions' rate (2x dense)")
     if ex is not None:
         line["config"]["output_stage"] = {"c_type": ex[0], "d_type": ex[1], "alpha": ex[2],
                                           "beta": ex[3]}
-    h.close()
+    del r
+    if name == "C2" and ex is None and not args.no_extra:
+        # the other input types the metric names, timed the same way (full-size
+        # inputs, every step the whole product)
+        others = {}
+        for o in EXTRA_WORKLOADS:
+            ro = time_workload(o, args.steps, args.warmup, args.reps, None, None, dev)
+            t_o, u_o, pk_o, roof_o, _ = roofline_of(o, ro)
+            others[o] = {"workload": synth.CONFIG_LABELS[o], "dtype": ro["p"].dtype,
+                         "plan": ro["label"], "value": round(t_o, 2), "unit": u_o,
+                         "ms_per_step": round(ro["ms"], 5),
+                         "rep_ms_per_step": [round(x, 5) for x in ro["rep_ms"]],
+                         "pct_of_dense_peak": round(100 * t_o / pk_o, 2), "roofline": roof_o,
+                         "parity": parity_sample(ro["p"], ro["D_host"])}
+            del ro
+            torch.cuda.empty_cache()
+        line["other_dtypes"] = others
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+        line["cpu_baseline"]["single_core_c1"] = single_core_c1()
     print(json.dumps(line), flush=True)
 
 

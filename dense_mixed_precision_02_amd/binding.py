@@ -163,7 +163,9 @@ _tls = threading.local()
 def default_handle() -> Handle:
     """The handle the torch front ends use: one per host thread, device and
     stream, since a handle's workspace must not serve two calls that can run at
-    the same time (one thread at a time, one stream at a time)."""
+    the same time (one thread at a time, one stream at a time).  Each cached
+    handle keeps its workspace until release_default_handles() is called on
+    the thread that created it (or the thread ends)."""
     import torch
     dev = torch.cuda.current_device()
     key = (dev, torch.cuda.current_stream(dev).cuda_stream)
@@ -175,6 +177,19 @@ def default_handle() -> Handle:
         h = Handle()
         handles[key] = h
     return h
+
+
+def release_default_handles() -> int:
+    """Close this thread's cached front-end handles and free their workspaces
+    (each close waits for its device's queued work).  A program that creates
+    many streams or threads calls this when it is done with one; the next
+    front-end call makes a new handle.  Returns the number of handles closed."""
+    handles = getattr(_tls, "handles", None) or {}
+    n = len(handles)
+    for h in handles.values():
+        h.close()
+    _tls.handles = {}
+    return n
 
 
 def _operand_layout(X, rows: int, cols: int, name: str):
@@ -226,8 +241,9 @@ def gemm(A, B, C=None, out=None, alpha: float = 1.0, beta: float = 1.0, out_dtyp
     if C is None:
         beta = 0.0
     else:
-        if C.device != A.device or C.dim() != nd or C.shape[-2:] != (M, N):
-            raise ValueError("C must be a tensor of shape (..., M, N) on A's GPU")
+        if C.device != A.device or C.dim() != nd or C.shape[-2:] != (M, N) or \
+                (nd == 3 and C.shape[0] != batch):
+            raise ValueError("C must be a tensor of shape ((batch,) M, N) on A's GPU")
         if C.stride(-1) != 1 or (M > 1 and C.stride(-2) < N):
             raise ValueError("C must be row-major with a row stride of at least N")
     c_code = _out_code(C.dtype if C is not None else acc)

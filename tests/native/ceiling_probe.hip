@@ -211,9 +211,15 @@ __global__ __launch_bounds__(256) void read_lds_direct(const char *buf, long lon
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long long chunk = 256 * 16 * 4;  // bytes per workgroup step
     const long long steps = bytes / chunk;
+    // The descriptor's base must sit in scalar registers: both halves of the
+    // (wave-uniform) address are read from the first lane.  The builtin returns
+    // a signed int, so each half is taken back to uint32_t before widening; a
+    // sign-extended low half would set the top bits of the base whenever bit 31
+    // of the address is set.
     const uint64_t a = (uint64_t)buf;
-    void *base = (void *)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
-                          __builtin_amdgcn_readfirstlane((uint32_t)a));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *base = (void *)(((uint64_t)hi << 32) | lo);
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff),
                                           0x00020000);
@@ -226,6 +232,8 @@ __global__ __launch_bounds__(256) void read_lds_direct(const char *buf, long lon
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rs, (__attribute__((address_space(3))) void *)(lds + wave * 4096 + q * 1024), 16,
                     off + q * 4096, 0, 0, 0);
+            // at most 16 copies of this wave in flight (vmcnt <= 12 before the next 4)
+            __builtin_amdgcn_s_waitcnt(12 | (0x7 << 4) | (0xf << 8));
         }
         __builtin_amdgcn_s_waitcnt(0);
     }

@@ -76,6 +76,11 @@ def test_cpu_baseline_record():
     assert "of the same seeded problem" in rec["sample"]
 
 
+def test_single_core_oracle_record():
+    rec = bench.single_core_c1()
+    assert rec["cores"] == 1 and rec["kind"] == "oracle" and rec["value"] > 0
+
+
 def check_line(line, metric_unit, config):
     d = json.loads(line)
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
@@ -125,11 +130,24 @@ def test_bench_default_line_with_cpu_baseline(capsys):
         pytest.skip("no GPU")
     with capsys.disabled():
         print("[bench] default workload, 20 steps", flush=True)
-    lines = run_bench(capsys, "--steps", "20", "--cpu-budget", "2")
+    lines = run_bench(capsys, "--steps", "20", "--warmup", "5", "--cpu-budget", "2")
     assert len(lines) == 1, lines
     d = check_line(lines[0], "TFLOP/s", "C2")
+    reps = d["config"]["rep_ms_per_step"]
+    assert len(reps) == d["config"]["repetitions"] == 5
+    assert d["ms_per_step"] == round(sorted(reps)[2], 5)
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["single_core_c1"]["cores"] == 1 and cb["single_core_c1"]["value"] > 0
+    # the fp16 and int8 products the metric names, timed in the same run
+    other = d["other_dtypes"]
+    assert set(other) == set(bench.EXTRA_WORKLOADS)
+    for name, unit in (("S1", "TFLOP/s"), ("C3", "TOP/s")):
+        o = other[name]
+        assert o["workload"] == synth.CONFIG_LABELS[name] and o["unit"] == unit
+        assert o["value"] > 0 and o["ms_per_step"] > 0 and len(o["rep_ms_per_step"]) == 5
+        assert o["roofline"]["bound"] == "mfma" and 0 < o["roofline"]["frac"] < 1
+        assert o["parity"]["ok"], o["parity"]
 
 
 @pytest.mark.gpu

@@ -242,6 +242,9 @@ def test_torch_front_end_rejects(handle):
         lambda: dmp.gemm(A, B, C.cpu()),                                          # device
         lambda: dmp.gemm(A[:, ::2], B[:16], C),                                   # strided k
         lambda: dmp.gemm(A, B, C, out=torch.empty(64, 48, device="cuda")[:, :47]),
+        # batched A and B with a C of one batch entry: C's batch extent must match
+        lambda: dmp.gemm(A.expand(3, 64, 32).contiguous(), B.expand(3, 32, 48).contiguous(),
+                         torch.zeros(1, 64, 48, device="cuda")),
     ]
     for i, f in enumerate(bad):
         with pytest.raises((ValueError, TypeError)):
@@ -286,6 +289,9 @@ def test_front_end_streams_get_their_own_workspace(handle):
     for p, D in zip(probs, outs):
         log(f"[streams] bf16 {p.M}x{p.N}x{p.K} {dmp.plan_label(p.M, p.N, p.K, p.lda, p.ldb, p.ldc, 1, 2)}")
         check_full(p, D.cpu().numpy().reshape(1, p.M, p.ldc))
+    # the two streams' cached handles (and their workspaces) are released on request
+    assert dmp.release_default_handles() >= 2
+    assert dmp.default_handle() is not h1
 
 
 @pytest.mark.parametrize("case", ["f16-subnormal-inputs", "bf16-subnormal-inputs",
