@@ -16,12 +16,12 @@ from __future__ import annotations
 
 from .binding import (GEMM_A_COLMAJOR, GEMM_A_SHARED, GEMM_B_COLMAJOR, GEMM_B_SHARED, GEMM_BF16, GEMM_F16, GEMM_F64, GEMM_I8,
                       GEMM_OUT_BF16, GEMM_OUT_F16, GEMM_OUT_F32, GEMM_OUT_F64, GEMM_OUT_I32,
-                      GemmError, Handle, Sparse24, default_handle, gemm, gemm_sparse24, lib_path, load_library,
+                      GEMM_ERR_SCRATCH, NOALLOC_SCRATCH_BYTES, GemmError, Handle, Sparse24, default_handle, gemm, gemm_sparse24, lib_path, load_library,
                       prune24, release_default_handles, sparse24_kp, sparse24_mp, plan_label, status_string,
                       EXPORTED_SYMBOLS)
 
 __all__ = ["GEMM_A_COLMAJOR", "GEMM_A_SHARED", "GEMM_B_COLMAJOR", "GEMM_B_SHARED", "GEMM_BF16", "GEMM_F16", "GEMM_F64", "GEMM_I8",
            "GEMM_OUT_BF16", "GEMM_OUT_F16", "GEMM_OUT_F32", "GEMM_OUT_F64", "GEMM_OUT_I32",
-           "GemmError", "Handle", "Sparse24", "default_handle", "gemm", "gemm_sparse24", "lib_path", "load_library",
+           "GEMM_ERR_SCRATCH", "NOALLOC_SCRATCH_BYTES", "GemmError", "Handle", "Sparse24", "default_handle", "gemm", "gemm_sparse24", "lib_path", "load_library",
            "prune24", "release_default_handles", "sparse24_kp", "sparse24_mp", "plan_label",
            "status_string", "EXPORTED_SYMBOLS"]

@@ -13,8 +13,10 @@ GEMM_A_COLMAJOR, GEMM_B_COLMAJOR, GEMM_A_SHARED, GEMM_B_SHARED = 1, 2, 4, 8
 GEMM_OUT_F32, GEMM_OUT_F16, GEMM_OUT_BF16, GEMM_OUT_I32, GEMM_OUT_F64 = 0, 1, 2, 3, 4
 GEMM_OK = 0
 
-EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_prune24",
+EXPORTED_SYMBOLS = ("gemm_create", "gemm_run", "gemm_run_ex", "gemm_run_noalloc", "gemm_prune24",
                     "gemm_run_sparse24", "gemm_destroy", "gemm_status_string", "gemm_plan")
+GEMM_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -55,6 +57,8 @@ def load_library():
         lib.gemm_run_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                     ctypes.c_int, ctypes.c_uint, i64, ctypes.c_float,
                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+        lib.gemm_run_noalloc.restype = ctypes.c_int
+        lib.gemm_run_noalloc.argtypes = lib.gemm_run_ex.argtypes
         lib.gemm_prune24.restype = ctypes.c_int
         lib.gemm_prune24.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, i64, vp, vp, vp]
         lib.gemm_run_sparse24.restype = ctypes.c_int
@@ -125,6 +129,14 @@ class Handle:
         """Raw-pointer call of gemm_run_ex; returns the status code."""
         return load_library().gemm_run_ex(self.ptr, A, B, C, D, M, N, K, lda, ldb, ldc, dtype,
                                           flags, batch, alpha, beta, c_type, d_type, stream)
+
+    def status_noalloc(self, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags=0, batch=1,
+                       alpha=1.0, beta=1.0, c_type=GEMM_OUT_F32, d_type=GEMM_OUT_F32,
+                       stream=0) -> int:
+        """Raw-pointer call of gemm_run_noalloc (fixed scratch, no device allocation);
+        returns the status code."""
+        return load_library().gemm_run_noalloc(self.ptr, A, B, C, D, M, N, K, lda, ldb, ldc, dtype,
+                                               flags, batch, alpha, beta, c_type, d_type, stream)
 
     def prune24(self, A, M, K, lda, dtype, batch, Ac, meta, stream=0) -> int:
         """Raw-pointer call of gemm_prune24; returns the status code."""

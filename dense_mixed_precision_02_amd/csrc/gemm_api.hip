@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/dmp_gemm.h"
@@ -171,6 +172,157 @@ hipError_t launch_tiny(const Plan &P, int dtype, const void *A, const void *B, c
     return launch_tiny_dt<I8>(P.cfg, t, sa, sb, P.grid, s);
 }
 
+// ---------------------------------------------------------------------------
+// Fixed scratch for gemm_run_noalloc: one array per device that loads this
+// library, held until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in for the symbol); the device
+// address of each device's copy is looked up once, with that device current,
+// and kept in scratch_ptr.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[GEMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_lock;
+void *scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of the current device's scratch (looked up on first use).
+hipError_t scratch_for(int dev, void **out) {
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(scratch_lock);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// gemm_run_ex and gemm_run_noalloc: the whole dense path.  ws_fixed == nullptr:
+// the handle's workspace, grown on demand; otherwise ws_fixed (ws_cap bytes),
+// and a plan that needs more fails with GEMM_ERR_SCRATCH before anything is
+// enqueued.
+int run_dense(gemm_handle_t h, const void *A, const void *B, const void *C, void *D, int64_t M,
+              int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+              unsigned flags, int64_t batch, const EpiParams &ep, void *stream, void *ws_fixed,
+              size_t ws_cap) {
+    int rc = validate(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, true, ep);
+    if (rc != GEMM_OK) return rc;
+    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
+    const bool a_sh = flags & GEMM_A_SHARED, b_sh = flags & GEMM_B_SHARED;
+    // (A and B are not read when K == 0, and their leading dimensions unchecked)
+    const int64_t sA = (a_sh || K == 0) ? 0 : (a_col ? K : M) * lda;
+    const int64_t sB = (b_sh || K == 0) ? 0 : (b_col ? N : K) * ldb;
+    const int64_t sC = M * ldc;
+    const Plan P = make_plan(h->num_cus, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
+    if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
+
+    if (P.copy_only)
+        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, ep, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+
+    if (P.cfg == CFG_TINY4 || P.cfg == CFG_TINY16)
+        return launch_tiny(P, dtype, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
+                           batch, ep, a_sh, b_sh, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+
+    if (dtype == GEMM_F64)
+        return launch_f64(P, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
+                          ep.use_c, s) == hipSuccess
+                   ? GEMM_OK
+                   : GEMM_ERR_HIP;
+
+    if (P.cfg == CFG_GENERIC) {
+        GenericArgs g;
+        g.A = A; g.B = B; g.C = C; g.D = D;
+        g.M = M; g.N = N; g.K = K;
+        g.a_rs = a_col ? 1 : lda;
+        g.a_ks = a_col ? lda : 1;
+        g.b_ks = b_col ? 1 : ldb;
+        g.b_cs = b_col ? ldb : 1;
+        g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
+        g.tiles_m = P.tiles_m; g.tiles_n = P.tiles_n;
+        g.ep = ep;
+        const dim3 grid((unsigned)P.grid), blk(64);
+        if (dtype == GEMM_F16) hipLaunchKernelGGL(generic_gemm<F16>, grid, blk, 0, s, g);
+        else if (dtype == GEMM_BF16) hipLaunchKernelGGL(generic_gemm<BF16>, grid, blk, 0, s, g);
+        else hipLaunchKernelGGL(generic_gemm<I8>, grid, blk, 0, s, g);
+        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+    }
+
+    void *ws = ws_fixed;
+    if (ws_fixed) {
+        if (P.ws_needed > ws_cap) return GEMM_ERR_SCRATCH;
+    } else if (P.ws_needed > h->ws_bytes) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return GEMM_ERR_INVALID_ARG;
+        if (h->ws) {
+            // the old workspace may still be read by queued work on some stream
+            if (hipDeviceSynchronize() != hipSuccess) return GEMM_ERR_HIP;
+            if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
+            h->ws = nullptr;
+            h->ws_bytes = 0;
+        }
+        if (hipMalloc(&h->ws, P.ws_needed) != hipSuccess) {
+            h->ws = nullptr;
+            (void)hipGetLastError();
+            return GEMM_ERR_ALLOC;
+        }
+        h->ws_bytes = P.ws_needed;
+    }
+    if (!ws_fixed) ws = h->ws;
+
+    const void *Bk = B;
+    int64_t ldbk = ldb, sBk = sB;
+    bool b_colk = b_col;
+    if (P.transpose_b) {
+        const int tk = (int)cdiv(K, 128), tn = (int)cdiv(N, 128);
+        const int64_t tgrid = (int64_t)tk * tn * batch;
+        if (tgrid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
+        const int vec_in = aligned16(B) && ldb % 16 == 0 && sB % 16 == 0;
+        hipLaunchKernelGGL(transpose_i8, dim3((unsigned)tgrid), dim3(256), 0, s, (const int8_t *)B, K,
+                           N, ldb, sB, (int8_t *)ws, P.ldt, N * P.ldt, tk, tn, vec_in);
+        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+        Bk = ws;
+        ldbk = P.ldt;
+        sBk = N * P.ldt;
+        b_colk = true;
+    }
+
+    TileArgs t;
+    t.A = A; t.B = Bk; t.C = C; t.D = D; t.W = ws;
+    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldbk; t.ldc = ldc;
+    t.sA = sA; t.sB = sBk; t.sC = sC;
+    t.k_chunk = P.k_chunk;
+    t.tiles_m = P.tiles_m; t.tiles_n = P.tiles_n;
+    t.batch = (int)batch; t.splits = P.splits;
+    t.partial = P.reduce ? 1 : 0;
+    t.ep = ep;
+    hipError_t e;
+    if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_colk, P.grid, s);
+    else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_colk, P.grid, s);
+    else e = launch_cfg<I8>(P.cfg, t, a_col, b_colk, P.grid, s);
+    if (e != hipSuccess) return GEMM_ERR_HIP;
+    if (P.reduce && launch_reduce(dtype, ws, C, D, M, N, ldc, batch, P.splits, ep, s) != hipSuccess)
+        return GEMM_ERR_HIP;
+    return GEMM_OK;
+}
+
+EpiParams make_epi(float alpha, float beta, int c_type, int d_type) {
+    EpiParams ep;
+    ep.alpha = alpha;
+    ep.beta = beta;
+    ep.c_type = c_type;
+    ep.d_type = d_type;
+    ep.use_c = beta != 0.0f;
+    return ep;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,6 +334,7 @@ const char *gemm_status_string(int status) {
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "GEMM_ERR_UNSUPPORTED_DEVICE";
     case GEMM_ERR_ALLOC: return "GEMM_ERR_ALLOC";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    case GEMM_ERR_SCRATCH: return "GEMM_ERR_SCRATCH";
     default: return "GEMM_ERR_UNKNOWN";
     }
 }
@@ -198,6 +351,12 @@ int gemm_create(gemm_handle_t *out) {
     if (!h) return GEMM_ERR_ALLOC;
     h->device = dev;
     h->num_cus = prop.multiProcessorCount;
+    // set-up of gemm_run_noalloc: this device's scratch address, once per device
+    void *sp = nullptr;
+    if (scratch_for(dev, &sp) != hipSuccess) {
+        delete h;
+        return GEMM_ERR_HIP;
+    }
     *out = h;
     return GEMM_OK;
 }
@@ -248,112 +407,23 @@ int gemm_run_ex(gemm_handle_t h, const void *A, const void *B, const void *C, vo
                 int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
                 unsigned flags, int64_t batch, float alpha, float beta, int c_type, int d_type,
                 void *stream) {
-    EpiParams ep;
-    ep.alpha = alpha;
-    ep.beta = beta;
-    ep.c_type = c_type;
-    ep.d_type = d_type;
-    ep.use_c = beta != 0.0f;
-    int rc = validate(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch, true, ep);
-    if (rc != GEMM_OK) return rc;
-    if (M == 0 || N == 0 || batch == 0) return GEMM_OK;
-    hipStream_t s = (hipStream_t)stream;
-    const bool a_col = flags & GEMM_A_COLMAJOR, b_col = flags & GEMM_B_COLMAJOR;
-    const bool a_sh = flags & GEMM_A_SHARED, b_sh = flags & GEMM_B_SHARED;
-    // (A and B are not read when K == 0, and their leading dimensions unchecked)
-    const int64_t sA = (a_sh || K == 0) ? 0 : (a_col ? K : M) * lda;
-    const int64_t sB = (b_sh || K == 0) ? 0 : (b_col ? N : K) * ldb;
-    const int64_t sC = M * ldc;
-    const Plan P = make_plan(h->num_cus, A, B, M, N, K, lda, ldb, dtype, flags, batch, true);
-    if (P.grid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;  // beyond one launch's grid
+    return run_dense(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch,
+                     make_epi(alpha, beta, c_type, d_type), stream, nullptr, 0);
+}
 
-    if (P.copy_only)
-        return launch_reduce(dtype, nullptr, C, D, M, N, ldc, batch, 0, ep, s) == hipSuccess
-                   ? GEMM_OK
-                   : GEMM_ERR_HIP;
-
-    if (P.cfg == CFG_TINY4 || P.cfg == CFG_TINY16)
-        return launch_tiny(P, dtype, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
-                           batch, ep, a_sh, b_sh, s) == hipSuccess
-                   ? GEMM_OK
-                   : GEMM_ERR_HIP;
-
-    if (dtype == GEMM_F64)
-        return launch_f64(P, A, B, C, D, M, N, K, lda, ldb, ldc, a_col, b_col, sA, sB, sC,
-                          ep.use_c, s) == hipSuccess
-                   ? GEMM_OK
-                   : GEMM_ERR_HIP;
-
-    if (P.cfg == CFG_GENERIC) {
-        GenericArgs g;
-        g.A = A; g.B = B; g.C = C; g.D = D;
-        g.M = M; g.N = N; g.K = K;
-        g.a_rs = a_col ? 1 : lda;
-        g.a_ks = a_col ? lda : 1;
-        g.b_ks = b_col ? 1 : ldb;
-        g.b_cs = b_col ? ldb : 1;
-        g.ldc = ldc; g.sA = sA; g.sB = sB; g.sC = sC;
-        g.tiles_m = P.tiles_m; g.tiles_n = P.tiles_n;
-        g.ep = ep;
-        const dim3 grid((unsigned)P.grid), blk(64);
-        if (dtype == GEMM_F16) hipLaunchKernelGGL(generic_gemm<F16>, grid, blk, 0, s, g);
-        else if (dtype == GEMM_BF16) hipLaunchKernelGGL(generic_gemm<BF16>, grid, blk, 0, s, g);
-        else hipLaunchKernelGGL(generic_gemm<I8>, grid, blk, 0, s, g);
-        return hipGetLastError() == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
-    }
-
-    if (P.ws_needed > h->ws_bytes) {
-        int cur = 0;
-        if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return GEMM_ERR_INVALID_ARG;
-        if (h->ws) {
-            // the old workspace may still be read by queued work on some stream
-            if (hipDeviceSynchronize() != hipSuccess) return GEMM_ERR_HIP;
-            if (hipFree(h->ws) != hipSuccess) return GEMM_ERR_HIP;
-            h->ws = nullptr;
-            h->ws_bytes = 0;
-        }
-        if (hipMalloc(&h->ws, P.ws_needed) != hipSuccess) {
-            h->ws = nullptr;
-            (void)hipGetLastError();
-            return GEMM_ERR_ALLOC;
-        }
-        h->ws_bytes = P.ws_needed;
-    }
-
-    const void *Bk = B;
-    int64_t ldbk = ldb, sBk = sB;
-    bool b_colk = b_col;
-    if (P.transpose_b) {
-        const int tk = (int)cdiv(K, 128), tn = (int)cdiv(N, 128);
-        const int64_t tgrid = (int64_t)tk * tn * batch;
-        if (tgrid > 0x7fffffff) return GEMM_ERR_INVALID_ARG;
-        const int vec_in = aligned16(B) && ldb % 16 == 0 && sB % 16 == 0;
-        hipLaunchKernelGGL(transpose_i8, dim3((unsigned)tgrid), dim3(256), 0, s, (const int8_t *)B, K,
-                           N, ldb, sB, (int8_t *)h->ws, P.ldt, N * P.ldt, tk, tn, vec_in);
-        if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
-        Bk = h->ws;
-        ldbk = P.ldt;
-        sBk = N * P.ldt;
-        b_colk = true;
-    }
-
-    TileArgs t;
-    t.A = A; t.B = Bk; t.C = C; t.D = D; t.W = h->ws;
-    t.M = M; t.N = N; t.K = K; t.lda = lda; t.ldb = ldbk; t.ldc = ldc;
-    t.sA = sA; t.sB = sBk; t.sC = sC;
-    t.k_chunk = P.k_chunk;
-    t.tiles_m = P.tiles_m; t.tiles_n = P.tiles_n;
-    t.batch = (int)batch; t.splits = P.splits;
-    t.partial = P.reduce ? 1 : 0;
-    t.ep = ep;
-    hipError_t e;
-    if (dtype == GEMM_F16) e = launch_cfg<F16>(P.cfg, t, a_col, b_colk, P.grid, s);
-    else if (dtype == GEMM_BF16) e = launch_cfg<BF16>(P.cfg, t, a_col, b_colk, P.grid, s);
-    else e = launch_cfg<I8>(P.cfg, t, a_col, b_colk, P.grid, s);
-    if (e != hipSuccess) return GEMM_ERR_HIP;
-    if (P.reduce && launch_reduce(dtype, h->ws, C, D, M, N, ldc, batch, P.splits, ep, s) != hipSuccess)
-        return GEMM_ERR_HIP;
-    return GEMM_OK;
+int gemm_run_noalloc(gemm_handle_t h, const void *A, const void *B, const void *C, void *D,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                     int dtype, unsigned flags, int64_t batch, float alpha, float beta, int c_type,
+                     int d_type, void *stream) {
+    if (!h) return GEMM_ERR_INVALID_ARG;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return GEMM_ERR_HIP;
+    if (cur != h->device) return GEMM_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    if (scratch_for(h->device, &ws) != hipSuccess) return GEMM_ERR_HIP;
+    return run_dense(h, A, B, C, D, M, N, K, lda, ldb, ldc, dtype, flags, batch,
+                     make_epi(alpha, beta, c_type, d_type), stream, ws,
+                     (size_t)GEMM_NOALLOC_SCRATCH_BYTES);
 }
 
 int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t lda, int dtype,

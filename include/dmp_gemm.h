@@ -102,9 +102,11 @@ typedef enum {
     GEMM_ERR_INVALID_ARG = 1,        /* null pointer, negative size, ld too small, bad dtype/flags */
     GEMM_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950; there is no fallback */
     GEMM_ERR_ALLOC = 3,              /* workspace allocation failed */
-    GEMM_ERR_HIP = 4                 /* a HIP API call or kernel launch reported an error; the
+    GEMM_ERR_HIP = 4,                /* a HIP API call or kernel launch reported an error; the
                                         launch status is read with hipGetLastError, so an error an
                                         earlier HIP call of this thread left unread is reported too */
+    GEMM_ERR_SCRATCH = 5             /* gemm_run_noalloc: the product needs more scratch than
+                                        GEMM_NOALLOC_SCRATCH_BYTES; nothing was enqueued */
 } gemm_status_t;
 
 /*
@@ -209,6 +211,28 @@ int gemm_prune24(gemm_handle_t h, const void *A, int64_t M, int64_t K, int64_t l
 int gemm_run_sparse24(gemm_handle_t h, const void *Ac, const void *meta, const void *B,
                       const void *C, void *D, int64_t M, int64_t N, int64_t K, int64_t ldb,
                       int64_t ldc, int dtype, unsigned flags, int64_t batch, void *stream);
+
+/*
+ * For callers that cannot allocate device memory while they run products: code
+ * that a HIP graph captures, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics, results (bit for bit) and errors as
+ * gemm_run_ex, but the split-K partials and the transposed copy of a row-major
+ * int8 B live in a fixed scratch array of GEMM_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * that the library holds on every device it runs on until the process ends;
+ * the call never allocates or frees device memory (the scratch address is
+ * looked up once per device by gemm_create).  A product whose plan needs more
+ * scratch fails with GEMM_ERR_SCRATCH and enqueues nothing (gemm_run_ex then
+ * serves it).  The current device must be the handle's (else
+ * GEMM_ERR_INVALID_ARG).  Every call on one device shares that device's
+ * scratch and leaves its contents behind: calls that can run at the same time
+ * on one device (different streams, threads or handles) race and must be
+ * ordered by the caller.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int gemm_run_noalloc(gemm_handle_t h, const void *A, const void *B, const void *C, void *D,
+                     int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                     int dtype, unsigned flags, int64_t batch, float alpha, float beta,
+                     int c_type, int d_type, void *stream);
 
 /* Release the handle's workspace (after synchronising its device) and the handle. */
 int gemm_destroy(gemm_handle_t h);

@@ -24,6 +24,12 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted(dmp.EXPORTED_SYMBOLS)
 
 
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GEMM_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == dmp.NOALLOC_SCRATCH_BYTES
+
+
 def test_header_is_plain_c():
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
                    check=True)
@@ -45,6 +51,7 @@ def test_status_strings():
     assert dmp.status_string(2) == "GEMM_ERR_UNSUPPORTED_DEVICE"
     assert dmp.status_string(3) == "GEMM_ERR_ALLOC"
     assert dmp.status_string(4) == "GEMM_ERR_HIP"
+    assert dmp.status_string(5) == "GEMM_ERR_SCRATCH"
     assert dmp.status_string(99) == "GEMM_ERR_UNKNOWN"
 
 
