@@ -14,6 +14,7 @@
 #include "dgemm.hpp"
 #include "sparse_gemm.hpp"
 #include "tile_gemm.hpp"
+#include "tile16_gemm.hpp"
 #include "tiny_gemm.hpp"
 #include "plan.hpp"
 
@@ -85,11 +86,23 @@ hipError_t launch_tile_layout(const TileArgs &a, bool a_col, bool b_col, int64_t
     return launch_tile<DT, E, E, false, false>(a, grid, s);
 }
 
+// 256x256 tiles: the 16x16-instruction kernel (tile16_gemm.hpp).
+template <class DT>
+hipError_t launch_tile16_layout(const TileArgs &a, bool a_col, bool b_col, int64_t grid,
+                                hipStream_t s) {
+    const dim3 g((unsigned)grid), blk(256);
+    if (!a_col && b_col) hipLaunchKernelGGL((tile16_gemm<DT, true, true>), g, blk, 0, s, a);
+    else if (!a_col && !b_col) hipLaunchKernelGGL((tile16_gemm<DT, true, false>), g, blk, 0, s, a);
+    else if (a_col && b_col) hipLaunchKernelGGL((tile16_gemm<DT, false, true>), g, blk, 0, s, a);
+    else hipLaunchKernelGGL((tile16_gemm<DT, false, false>), g, blk, 0, s, a);
+    return hipGetLastError();
+}
+
 template <class DT>
 hipError_t launch_cfg(int cfg, const TileArgs &a, bool a_col, bool b_col, int64_t grid,
                       hipStream_t s) {
     switch (cfg) {
-    case CFG_L: return launch_tile_layout<DT, 256>(a, a_col, b_col, grid, s);
+    case CFG_L: return launch_tile16_layout<DT>(a, a_col, b_col, grid, s);
     case CFG_M: return launch_tile_layout<DT, 128>(a, a_col, b_col, grid, s);
     default: return launch_tile_layout<DT, 64>(a, a_col, b_col, grid, s);
     }

@@ -54,14 +54,20 @@ __device__ static inline int cols_in(int64_t N, int64_t gcol) {
 // even/odd rows of any 16) map to distinct 16-byte slots modulo 128 (256) bytes.
 __device__ static inline int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-template <class DT, int R, int NW, bool KCONTIG>
+// PAD (MN-contiguous operands only): bytes of padding after each row of
+// 128-byte blocks (a "block row": 4 k-rows (16-bit) or 8 k-rows (int8) of all
+// R rows), so that reads of blocks in consecutive block rows fall on different
+// LDS banks; every block row is a whole number of 1 KB copies (R >= 128).
+template <class DT, int R, int NW, bool KCONTIG, int PAD = 0>
 struct Operand {
     // R rows per tile, NW waves in the workgroup.
     static constexpr int ESZ = DT::ESZ;
     static constexpr int G = DT::G;
     static constexpr int KT = 128 / ESZ;            // k-tile in elements
-    static constexpr int BYTES = R * 128;           // one LDS buffer
-    static constexpr int CHUNKS = BYTES / 1024;     // 1 KB per wave-wide load
+    static_assert(PAD == 0 || (!KCONTIG && R >= 128 && PAD % 16 == 0), "padding: MN-contiguous, R >= 128");
+    static constexpr int ROW_BYTES = R * 8 + PAD;   // one block row (R / 16 blocks) with its padding
+    static constexpr int BYTES = R * 128 + 16 * PAD;  // one LDS buffer (16 block rows per k-tile)
+    static constexpr int CHUNKS = R * 128 / 1024;   // 1 KB per wave-wide load
     static_assert(CHUNKS % NW == 0, "chunks must split evenly over waves");
     static constexpr int CPW = CHUNKS / NW;         // chunks per wave
     static constexpr int KB = (ESZ == 2) ? 4 : 8;   // k-rows per 128-byte block (MN-contig)
@@ -113,8 +119,16 @@ struct Operand {
         bool ok;
         if (KCONTIG) ok = (row_or_k + 8 * NW * j < Rtot) && (fixed < kleft);
         else ok = (fixed < Rtot) && (row_or_k + KSTEP * j < kleft);
-        load_granule_to_lds<CPOL>(rs, lds + c * 1024, ok ? off0 + j * step : OOB_OFFSET);
+        load_granule_to_lds<CPOL>(rs, lds + chunk_offset(c), ok ? off0 + j * step : OOB_OFFSET);
     }
+
+    // LDS byte offset of copy chunk c (1 KB; R / 128 chunks per block row).
+    __device__ static constexpr int chunk_offset(int c) {
+        if constexpr (PAD == 0) return c * 1024;
+        else return (c / (R / 128)) * ROW_BYTES + (c % (R / 128)) * 1024;
+    }
+    // LDS byte offset of 128-byte block (kb, mb) of an MN-contiguous panel.
+    __device__ static constexpr int block_offset(int kb, int mb) { return kb * ROW_BYTES + mb * 128; }
 
     // LDS reads one fragment takes
     static constexpr int READS = KCONTIG ? 1 : 2;
