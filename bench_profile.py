@@ -172,6 +172,31 @@ def cmd_counters(a):
     sys.stdout.write(text)
 
 
+def cmd_ceiling(a):
+    """The JSON lines of `bench.py --ceiling` as a table."""
+    import json
+    rows = [json.loads(x) for x in open(a.jsonl) if x.startswith("{")]
+    lines = ["# Practical ceilings of this MI355X (tests/native/ceiling_probe.hip)", "",
+             f"command: {a.cmd}", "",
+             "Matrix instructions alone (independent accumulators, operands in registers,",
+             "one workgroup of four waves per CU unless stated); rate = operations / launch time,",
+             "median of the timed launches; clock = shader-clock counter ticks / launch time.", "",
+             f"{'probe':<28} {'waves/SIMD':>10} {'rate':>10} {'unit':>8} {'of datasheet':>13} {'clock GHz':>10}"]
+    for r in rows:
+        if "frac_of_datasheet" in r:
+            lines.append(f"{r['probe']:<28} {r['waves_per_simd']:>10} {r['rate']:>10.1f} {r['unit']:>8} "
+                         f"{100 * r['frac_of_datasheet']:>12.1f}% {r['clock_counter_ghz']:>10.2f}")
+    lines += ["", "Bandwidth (L2-resident 1 MB buffer swept by every workgroup; LDS; HBM streams of 2 GiB):", "",
+              f"{'probe':<28} {'workgroups/CU':>13} {'rate':>10} {'unit':>6}"]
+    for r in rows:
+        if "frac_of_datasheet" not in r:
+            wg = r.get("workgroups_per_cu", "")
+            lines.append(f"{r['probe']:<28} {str(wg):>13} {r['rate']:>10.2f} {r['unit']:>6}")
+    text = "\n".join(lines) + "\n"
+    open(a.out, "w").write(text)
+    sys.stdout.write(text)
+
+
 def read_traffic(path: str):
     """(bytes per launch, source hash) from a traffic summary, or None."""
     if not os.path.exists(path):
@@ -206,8 +231,13 @@ def main():
     c.add_argument("--cmd", required=True)
     c.add_argument("--out", required=True)
     c.add_argument("--us", type=float, default=None, help="launch duration, for the clock")
+    e = sub.add_parser("ceiling")
+    e.add_argument("jsonl")
+    e.add_argument("--cmd", required=True)
+    e.add_argument("--out", required=True)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "counters": cmd_counters,
+     "ceiling": cmd_ceiling}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -64,14 +64,18 @@ __device__ static inline void mma_drain() {
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::);
 }
 
-// 16-byte fragment of MFMA step s (0 or 1; 4 granules of the 8-granule
-// k-tile) for rows [rbase, rbase + 16): lane L gets row rbase + L % 16 and
-// granule 4 s + L / 16.
+// 16-byte fragment of MFMA step s (0 or 1) for rows [rbase, rbase + 16): lane L
+// gets row rbase + L % 16 and granule 2 (L / 16) + s of the 8-granule k-tile.
+// Which granules a step takes is free as long as A and B agree (each step sums
+// over its four granules, and the two steps over all eight); this order puts
+// the four 16-lane groups of one read on granules two apart, which keeps the
+// reads free of LDS bank conflicts (granules 4 s + L / 16 gave conflicts on
+// about half of the LDS cycles).
 template <class DT, class Op, int R, bool KCONTIG>
 __device__ static inline intx4 frag16(const DMP_LDS char *lds, int rbase, int s, int lane) {
     if constexpr (KCONTIG) {
         const int row = rbase + (lane & 15);
-        const int g = 4 * s + (lane >> 4);
+        const int g = 2 * (lane >> 4) + s;
         return *(const DMP_LDS intx4 *)(lds + row * 128 + ((g ^ swz(row)) << 4));
     } else {
         // MN-contiguous panels: 128-byte blocks of 4 k-rows (16-bit) or 8 k-rows
@@ -82,7 +86,7 @@ __device__ static inline intx4 frag16(const DMP_LDS char *lds, int rbase, int s,
         if constexpr (DT::ESZ == 2) {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int kb = 8 * s + 2 * grp + t;  // block of k-rows 4 kb .. 4 kb + 3
+                const int kb = 2 * (2 * grp + s) + t;  // granule 2 grp + s: blocks 2 g, 2 g + 1
                 const int addr = Op::block_offset(kb, rbase >> 4) + j * 8;
                 shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DMP_LDS shortx4 *)(lds + addr));
                 intx2 w = __builtin_bit_cast(intx2, v);
@@ -92,7 +96,7 @@ __device__ static inline intx4 frag16(const DMP_LDS char *lds, int rbase, int s,
         } else {
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int kb = 8 * s + 2 * grp + t;  // block of k-rows 8 kb .. 8 kb + 7
+                const int kb = 2 * (2 * grp + s) + t;  // granule 2 grp + s: blocks 2 g, 2 g + 1
                 const int addr = Op::block_offset(kb, rbase >> 4) + j * 8;
                 intx2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DMP_LDS intx2 *)(lds + addr));
                 out[2 * t] = w[0];
@@ -110,11 +114,14 @@ __global__ __launch_bounds__(256) void tile16_gemm(const TileArgs p) {
     constexpr int TM = WTM / 16, TN = WTN / 16;  // 8 x 8 instructions per step
     constexpr int KT = 128 / DT::ESZ;            // k-tile in elements
     // An MN-contiguous panel is read four blocks at a time (one per 16-lane
-    // group), from block rows two apart; 64 bytes of padding per block row put
-    // them on alternate halves of the banks (without it all four share one half
-    // and each read takes twice the cycles).
-    using OpA = Operand<DT, BM, NW, AK, AK ? 0 : 64>;
-    using OpB = Operand<DT, BN, NW, BKC, BKC ? 0 : 64>;
+    // group), from block rows four apart.  The LDS serves the groups in pairs
+    // (0 with 1, 2 with 3), and a pair is free of bank conflicts when its two
+    // 128-byte blocks fill the two halves of the 256 bytes of banks: 32 bytes
+    // of padding per block row (2080-byte rows, four of them 128 bytes past a
+    // multiple of 256) does that (16 bytes of padding, which puts the four 64
+    // bytes apart, left 31 % of the LDS cycles in bank conflicts).
+    using OpA = Operand<DT, BM, NW, AK, AK ? 0 : 32>;
+    using OpB = Operand<DT, BN, NW, BKC, BKC ? 0 : 32>;
     using acc_t = typename DT::acc;
     using acc4 = vec4_of<acc_t>;
     static_assert(OpA::CPW + OpB::CPW == 16, "16 copies per wave per k-tile");
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(256) void tile16_gemm(const TileArgs p) {
     __syncthreads();  // every wave is done with the operand buffers
     DMP_LDS char *slab_c = wave == 0 ? LA[0] : wave == 1 ? LB[0] : wave == 2 ? LA[1] : LB[1];
     DMP_LDS acc_t *slab = (DMP_LDS acc_t *)slab_c;
-    constexpr int SP = WTN + 8;  // padded slab row (elements)
+    constexpr int SP = WTN + 4;  // padded slab row (elements): rows 4 apart fall 16 banks apart
     static_assert(32 * SP * 4 <= OpA::BYTES && 32 * SP * 4 <= OpB::BYTES, "slab must fit");
     constexpr int LPR = WTN / 4;   // lanes per slab row (4 elements each)
     constexpr int RPP = 64 / LPR;  // slab rows per pass
