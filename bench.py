@@ -53,11 +53,11 @@ COPY_BYTES = 512 << 20
 # rocprofv3 HBM-traffic summary of the dominant kernel of each workload
 TRAFFIC_FILES = {
     "C1": "profiles/tile_gemm_f16_256x256x256_traffic.md",
-    "C2": "profiles/tile_gemm_bf16_4096x4096x4096_traffic.md",
-    "C3": "profiles/tile_gemm_i8_8192x8192x8192_traffic.md",
+    "C2": "profiles/tile16_gemm_bf16_4096x4096x4096_traffic.md",
+    "C3": "profiles/tile16_gemm_i8_8192x8192x8192_traffic.md",
     "C4": "profiles/tile_gemm_f16_batch8192_64x64x64_traffic.md",
-    "C5": "profiles/tile_gemm_splitk_bf16_1024x1024x65536_traffic.md",
-    "S1": "profiles/tile_gemm_f16_4096x4096x4096_traffic.md",
+    "C5": "profiles/tile16_gemm_splitk_bf16_1024x1024x65536_traffic.md",
+    "S1": "profiles/tile16_gemm_f16_4096x4096x4096_traffic.md",
     "F1": "profiles/dgemm_tile_f64_4096x4096x4096_traffic.md",
     "SP1": "profiles/sparse_gemm_bf16_4096x4096x4096_traffic.md",
     "SP2": "profiles/sparse_gemm_i8_8192x8192x8192_traffic.md",
@@ -325,12 +325,18 @@ def ceiling_probes(quick: bool = False, target_ms: float = 20.0, launches: int =
     return out
 
 
-def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None):
-    """Upload workload `name`, run `warmup` untimed steps, then `reps` repetitions
-    of exactly `steps` timed steps each (HIP events on the launch stream, with a
-    device synchronisation before and after each repetition).  One step is one
-    call of the library on the whole problem.  Returns a dict with the problem,
-    the per-repetition times, the median, the plan label and the last output."""
+def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None, settle_ms=0.0,
+                  zero_operands=False):
+    """Upload workload `name`, run `warmup` untimed steps, then untimed steps for
+    at least `settle_ms` more milliseconds (the clock settle described at
+    SETTLE_MS), then `reps` repetitions of exactly `steps` timed steps each (HIP
+    events on the launch stream, with a device synchronisation before and after
+    each repetition).  One step is one call of the library on the whole problem.
+    Returns a dict with the problem, the per-repetition times, the median, the
+    plan label, the number of settle steps and the last output.  zero_operands:
+    A and B are all zeros (the same shapes, kernels and memory traffic; the
+    matrix units' inputs never change), for measuring how the operands' values
+    move the clock."""
     import numpy as np
     import torch
 
@@ -338,6 +344,9 @@ def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None
     import synth
 
     p = synth.config_problem(name)
+    if zero_operands:
+        p.A[...] = 0
+        p.B[...] = 0
 
     def up(x):
         t = torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x)
@@ -415,6 +424,21 @@ def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    settle_steps = 0
+    if settle_ms > 0:
+        # batches of launches of about 20 ms, sized from one synchronised step
+        t_w = time.perf_counter()
+        step(warmup)
+        torch.cuda.synchronize()
+        settle_steps = 1
+        per = (time.perf_counter() - t_w) * 1e3
+        batch = max(1, min(4096, int(20.0 / max(per, 1e-3))))
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < settle_ms:
+            for i in range(batch):
+                step(warmup + settle_steps + i)
+            torch.cuda.synchronize()
+            settle_steps += batch
     rep_ms = []
     t_all = time.perf_counter()
     for r in range(reps):
@@ -433,7 +457,7 @@ def time_workload(name, steps, warmup, reps, ex_args=None, rotate=None, dev=None
     h.close()
     return {"p": p, "ex": ex, "sparse": sparse, "label": label, "nsets": nsets,
             "rep_ms": rep_ms, "ms": float(np.median(rep_ms)), "wall": wall, "D_host": D_host,
-            "prune_us": prune_us}
+            "prune_us": prune_us, "settle_steps": settle_steps}
 
 
 def roofline_of(name, r):
@@ -458,6 +482,17 @@ def roofline_of(name, r):
         roof["traffic"] = round(rt[0])
     return tflops, unit, peak, roof, nbytes
 
+
+# Clock settle.  Once a sustained matrix-instruction load starts, this part's
+# power management moves the shader clock for some milliseconds before it holds
+# steady, and repetitions timed in that transient are slow and scattered (on the
+# 4096^3 bf16 product, 20-step repetitions right after a 5-step warm-up read 116
+# to 135 us per step, against about 105 us in a continuous run).  After the requested warm-up steps the
+# bench therefore keeps running untimed steps for SETTLE_MS more milliseconds
+# (reported as config.settle_ms and config.settle_steps), so that the timed
+# steps see the clock a continuously loaded device holds.  --settle-ms 0 turns
+# it off.
+SETTLE_MS = 300.0
 
 # Workloads timed beside the headline one in the default run, so that every input
 # type the metric names is measured: the 4096^3 fp16 product and the 8192^3 int8 one.
@@ -484,7 +519,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--reps", type=int, default=5,
                     help="repetitions of the timed steps; the line reports the median")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed steps for this many milliseconds after the warm-up steps")
     ap.add_argument("--config", default="C2")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="A and B all zeros (a study of how operand values move the clock; "
+                         "never the headline)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-extra", action="store_true",
                     help=f"skip the workloads timed beside the default one ({', '.join(EXTRA_WORKLOADS)})")
@@ -531,7 +571,8 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ex_args = (args.c_type, args.d_type, args.alpha, args.beta) if args.d_type else None
-    r = time_workload(name, args.steps, args.warmup, args.reps, ex_args, args.rotate, dev)
+    r = time_workload(name, args.steps, args.warmup, args.reps, ex_args, args.rotate, dev,
+                      args.settle_ms, args.zero_operands)
     p, ex, sparse, ms = r["p"], r["ex"], r["sparse"], r["ms"]
     tflops, unit, peak, roof, nbytes = roofline_of(name, r)
     line = {
@@ -554,10 +595,14 @@ def main(argv=None):
                    "hbm_gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
                    "repetitions": args.reps,
                    "rep_ms_per_step": [round(x, 5) for x in r["rep_ms"]],
-                   "timed_wall_s": round(r["wall"], 3), "input_sets": r["nsets"]},
+                   "timed_wall_s": round(r["wall"], 3), "input_sets": r["nsets"],
+                   "settle_ms": args.settle_ms, "settle_steps": r["settle_steps"]},
         "roofline": roof,
         "parity": parity_sample(p, r["D_host"], ex, sparse),
     }
+    if args.zero_operands:
+        line["data"] = "synthetic, A and B all zeros"
+        line["config"]["zero_operands"] = True
     if sparse:
         line["config"]["prune_us"] = round(r["prune_us"], 1)
         line["config"]["note"] = ("value = 2*M*N*K / time, the dense-equivalent rate of the 2:4 "
@@ -566,17 +611,19 @@ def main(argv=None):
         line["config"]["output_stage"] = {"c_type": ex[0], "d_type": ex[1], "alpha": ex[2],
                                           "beta": ex[3]}
     del r
-    if name == "C2" and ex is None and not args.no_extra:
+    if name == "C2" and ex is None and not args.no_extra and not args.zero_operands:
         # the other input types the metric names, timed the same way (full-size
         # inputs, every step the whole product)
         others = {}
         for o in EXTRA_WORKLOADS:
-            ro = time_workload(o, args.steps, args.warmup, args.reps, None, None, dev)
+            ro = time_workload(o, args.steps, args.warmup, args.reps, None, None, dev,
+                               args.settle_ms)
             t_o, u_o, pk_o, roof_o, _ = roofline_of(o, ro)
             others[o] = {"workload": synth.CONFIG_LABELS[o], "dtype": ro["p"].dtype,
                          "plan": ro["label"], "value": round(t_o, 2), "unit": u_o,
                          "ms_per_step": round(ro["ms"], 5),
                          "rep_ms_per_step": [round(x, 5) for x in ro["rep_ms"]],
+                         "settle_steps": ro["settle_steps"],
                          "pct_of_dense_peak": round(100 * t_o / pk_o, 2), "roofline": roof_o,
                          "parity": parity_sample(ro["p"], ro["D_host"])}
             del ro
