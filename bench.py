@@ -483,16 +483,17 @@ def roofline_of(name, r):
     return tflops, unit, peak, roof, nbytes
 
 
-# Clock settle.  Once a sustained matrix-instruction load starts, this part's
-# power management moves the shader clock for some milliseconds before it holds
-# steady, and repetitions timed in that transient are slow and scattered (on the
-# 4096^3 bf16 product, 20-step repetitions right after a 5-step warm-up read 116
-# to 135 us per step, against about 105 us in a continuous run).  After the requested warm-up steps the
-# bench therefore keeps running untimed steps for SETTLE_MS more milliseconds
-# (reported as config.settle_ms and config.settle_steps), so that the timed
-# steps see the clock a continuously loaded device holds.  --settle-ms 0 turns
-# it off.
-SETTLE_MS = 300.0
+# Clock settle (a study switch, off by default).  Once a sustained
+# matrix-instruction load starts, this part's power management moves the shader
+# clock for some milliseconds before it holds steady, and repetitions timed in
+# that transient are slow and scattered (on the 4096^3 bf16 product, 20-step
+# repetitions right after a 5-step warm-up read 116 to 135 us per step, against
+# about 105 us in a continuous run).  The default line keeps exactly the
+# requested warm-up and times what follows it.  --settle-ms T adds untimed steps
+# for T more milliseconds after the warm-up (reported as config.settle_ms and
+# config.settle_steps), for comparisons of steady-state rates; such a line is a
+# study, not the benchmark.
+SETTLE_MS = 0.0
 
 # Workloads timed beside the headline one in the default run, so that every input
 # type the metric names is measured: the 4096^3 fp16 product and the 8192^3 int8 one.
@@ -520,7 +521,8 @@ def main(argv=None):
     ap.add_argument("--reps", type=int, default=5,
                     help="repetitions of the timed steps; the line reports the median")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
-                    help="untimed steps for this many milliseconds after the warm-up steps")
+                    help="study switch: untimed steps for this many milliseconds after the "
+                         "warm-up steps (default 0: the line's warm-up is exactly --warmup)")
     ap.add_argument("--config", default="C2")
     ap.add_argument("--zero-operands", action="store_true",
                     help="A and B all zeros (a study of how operand values move the clock; "

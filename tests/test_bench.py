@@ -136,8 +136,8 @@ def test_bench_default_line_with_cpu_baseline(capsys):
     reps = d["config"]["rep_ms_per_step"]
     assert len(reps) == d["config"]["repetitions"] == 5
     assert d["ms_per_step"] == round(sorted(reps)[2], 5)
-    # untimed steps after the warm-up until the clock has settled
-    assert d["config"]["settle_ms"] == bench.SETTLE_MS and d["config"]["settle_steps"] > 0
+    # the warm-up is exactly the requested one: no untimed steps beyond it
+    assert d["config"]["settle_ms"] == 0 and d["config"]["settle_steps"] == 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert cb["single_core_c1"]["cores"] == 1 and cb["single_core_c1"]["value"] > 0
@@ -148,7 +148,7 @@ def test_bench_default_line_with_cpu_baseline(capsys):
         o = other[name]
         assert o["workload"] == synth.CONFIG_LABELS[name] and o["unit"] == unit
         assert o["value"] > 0 and o["ms_per_step"] > 0 and len(o["rep_ms_per_step"]) == 5
-        assert o["settle_steps"] > 0
+        assert o["settle_steps"] == 0
         assert o["roofline"]["bound"] == "mfma" and 0 < o["roofline"]["frac"] < 1
         assert o["parity"]["ok"], o["parity"]
 
