@@ -140,6 +140,17 @@ def cpu_baseline(p, budget_s: float = 15.0):
             "sample": f"{what} of the same seeded problem ({fl / 2:.3g} MACs, {dt:.1f} s)"}
 
 
+def _err_over_bound(err, tol):
+    """Largest error / bound over the sampled positions; an exact result counts 0 even where
+    the bound is 0 (a zero row of A or column of B with a zero C)."""
+    import numpy as np
+    err = np.asarray(err, dtype=np.float64)
+    tol = np.asarray(tol, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(err == 0, 0.0, err / tol)
+    return float(np.max(r))
+
+
 def parity_sample(p, D_host, ex=None, sparse=False):
     """Oracle check of the benchmarked output at sampled positions (not timed)."""
     import numpy as np
@@ -159,7 +170,7 @@ def parity_sample(p, D_host, ex=None, sparse=False):
              if c_type != "none" else np.zeros(n))
         Dref = oracle.scaled_reference(P, c, alpha, beta)
         tol = oracle.scaled_tolerance(p.K, S, c, Dref, alpha, beta, d_type)
-        ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+        ratio = _err_over_bound(np.abs(Dg.astype(np.float64) - Dref), tol)
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     if sparse:
         pruned = oracle.prune24(p.dtype, p.A, p.M, p.K, p.lda, p.batch)
@@ -169,12 +180,12 @@ def parity_sample(p, D_host, ex=None, sparse=False):
             return {"checked": n, "exact": ok, "ok": ok}
         Dref, S = r
         tol = oracle.float_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
-        ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+        ratio = _err_over_bound(np.abs(Dg.astype(np.float64) - Dref), tol)
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     if p.dtype == "f64":
         Dh, Dl, S = oracle.gemm_f64_points(p.A, p.B, p.C, pts, **p.oracle_args())
         tol = oracle.f64_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
-        ratio = float(np.max(oracle.f64_error(Dg, Dh, Dl) / tol))
+        ratio = _err_over_bound(oracle.f64_error(Dg, Dh, Dl), tol)
         return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
     r = oracle.gemm_points(p.dtype, p.A, p.B, p.C, pts, **p.oracle_args())
     if p.dtype == "i8":
@@ -182,7 +193,7 @@ def parity_sample(p, D_host, ex=None, sparse=False):
         return {"checked": n, "exact": ok, "ok": ok}
     Dref, S = r
     tol = oracle.float_tolerance(p.K, S, p.C[pts[:, 0], pts[:, 1], pts[:, 2]])
-    ratio = float(np.max(np.abs(Dg.astype(np.float64) - Dref) / tol))
+    ratio = _err_over_bound(np.abs(Dg.astype(np.float64) - Dref), tol)
     return {"checked": n, "max_err_over_bound": ratio, "ok": ratio <= 1.0}
 
 

@@ -160,3 +160,21 @@ def test_smoke_entry_point():
         pytest.skip("no GPU")
     import __graft_entry__
     __graft_entry__.smoke()  # raises on a mismatch against the oracle
+
+
+def test_parity_ratio_of_exact_zero_results():
+    """A zero row of A (or all-zero operands) with a zero C gives a zero bound; an exact result
+    there counts as error 0, a wrong one as infinitely far outside the bound."""
+    import numpy as np
+    assert bench._err_over_bound([0.0, 1e-9], [0.0, 1e-6]) == 1e-3
+    assert bench._err_over_bound([0.0, 0.0], [0.0, 0.0]) == 0.0
+    assert bench._err_over_bound([1e-30], [0.0]) == float("inf")
+    p = synth.config_problem("C1")
+    p.A[...] = 0
+    p.B[...] = 0
+    p.C[...] = 0
+    D = np.zeros((p.batch, p.M, p.ldc), dtype=np.float32)
+    r = bench.parity_sample(p, D)
+    assert r["ok"] and r["max_err_over_bound"] == 0.0
+    D[...] = 1e-30
+    assert not bench.parity_sample(p, D)["ok"]
