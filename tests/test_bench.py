@@ -123,6 +123,24 @@ def test_bench_line_on_gpu(capsys, config, extra, unit):
 
 
 @pytest.mark.gpu
+def test_bench_study_switches(capsys):
+    """--zero-operands labels its line and still checks parity (an exact zero result under a
+    zero bound); --settle-ms adds untimed steps and says how many."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with capsys.disabled():
+        print("[bench] study switches on the 256^3 fp16 workload", flush=True)
+    lines = run_bench(capsys, "--config", "C1", "--steps", "5", "--warmup", "2", "--no-cpu",
+                      "--zero-operands", "--settle-ms", "20")
+    assert len(lines) == 1, lines
+    d = json.loads(lines[0])
+    assert d["data"] == "synthetic, A and B all zeros" and d["config"]["zero_operands"]
+    assert d["parity"]["ok"], d["parity"]
+    assert d["config"]["settle_ms"] == 20 and d["config"]["settle_steps"] > 0
+
+
+@pytest.mark.gpu
 def test_bench_default_line_with_cpu_baseline(capsys):
     """The driver's invocation (default workload), with the CPU-oracle leg."""
     import torch
