@@ -204,15 +204,6 @@ __global__ __launch_bounds__(256) void tile16_gemm(const TileArgs p) {
     DMP_LDS char *LA[2] = {(DMP_LDS char *)lds_a0, (DMP_LDS char *)lds_a1};
     DMP_LDS char *LB[2] = {(DMP_LDS char *)lds_b0, (DMP_LDS char *)lds_b1};
 
-    // Per k-tile kt in buffer cur (the next one in the other buffer, nxt):
-    //   step 0: 64 instructions on fragment set 0; between them the 16
-    //           fragments of step 1 (from cur) are read into set 1;
-    //   wait for this wave's copies (k-tile kt+1) and meet every wave: kt+1 is
-    //           in nxt, and no wave reads cur any more;
-    //   step 1: 64 instructions on set 1; between them the fragments of step 0
-    //           of kt+1 (from nxt) are read into set 0, and the 16 copies of
-    //           k-tile kt+2 into cur are issued.
-    // So each copy has about two steps to land before the wait that needs it.
     // Fragment sets.  A K-contiguous operand's fragments of the next step are
     // read while the current step runs, into the other of two sets.  An
     // MN-contiguous operand's are read with the transposing LDS reads, which

@@ -419,7 +419,7 @@ __global__ __launch_bounds__(WM *WN * 64) void tile_gemm(const TileArgs p) {
     auto epilogue = [&](auto cs_c, auto ds_c) {
         constexpr int CS = decltype(cs_c)::value, DS = decltype(ds_c)::value;
         // 4-element vector accesses need every row start aligned to 4 elements
-        const bool vec_ok = (ldo % 4 == 0) && (CS == 0 || (uintptr_t)Cb % (4 * CS) == 0) &&
+        const bool vec_ok = (ldo % 4 == 0) && (CS == 0 || (uintptr_t)Cb % (4 * (CS ? CS : 1)) == 0) &&
                             (uintptr_t)Ob % (4 * DS) == 0;
         const int64_t row_w = m0 + wm * WTM;
         if constexpr (TM > 1) {
