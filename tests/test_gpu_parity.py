@@ -79,6 +79,23 @@ def test_ragged_shapes_all_layouts(handle, dtype, a_col, b_col):
             check_full(p, gpu_result(handle, p))
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("a_col,b_col", [(False, False), (False, True), (True, False), (True, True)])
+def test_tile256_ragged_edges(handle, dtype, a_col, b_col):
+    """The 256x256 tile with partial tiles on both edges and a last k-tile that is only part
+    full (K not a multiple of the k-tile), for every operand layout, compared in full."""
+    import dense_mixed_precision_02_amd as dmp
+    M, N = 4000, 4112  # 16 x 17 tiles, both edges partial
+    K = 1008 if dtype == "i8" else 1000  # 7.9 int8 / 15.6 16-bit k-tiles
+    p = synth.make_problem(dtype, M, N, K, a_col=a_col, b_col=b_col, seed=31,
+                           c_range=(-1.0, 1.0) if dtype != "i8" else (-(1 << 20), 1 << 20))
+    flags = (dmp.GEMM_A_COLMAJOR if a_col else 0) | (dmp.GEMM_B_COLMAJOR if b_col else 0)
+    lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, DTYPE_CODE[dtype], flags)
+    log(f"[tile256 edges] {dtype} a_col={a_col} b_col={b_col} {M}x{N}x{K} {lbl}")
+    assert lbl.startswith("tile256x256") and "splitk=1 " in lbl, lbl
+    check_full(p, gpu_result(handle, p))
+
+
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
 def test_generic_path_odd_k_and_unaligned(handle, dtype):
     """K not a multiple of the 16-byte granule, odd leading dimensions, and operands at
