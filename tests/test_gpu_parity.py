@@ -140,6 +140,27 @@ def test_split_k(handle, dtype):
         check_full(e, gpu_result(handle, e), exact=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "i8"])
+def test_tile256_batched_and_batched_split_k(handle, dtype):
+    """Batch entries on the 256x256 tile (one tile per workgroup across four 2048^2 products)
+    and split-K over a batch of two skinny products, compared in full; the exact-integer
+    inputs must come out bit for bit."""
+    import dense_mixed_precision_02_amd as dmp
+    for (M, N, K, batch, want) in [(2048, 2048, 512, 4, "splitk=1 "), (512, 512, 8192, 2, "splitk=")]:
+        p = synth.make_problem(dtype, M, N, K, batch=batch, seed=41,
+                               c_range=(-1.0, 1.0) if dtype != "i8" else (-(1 << 20), 1 << 20))
+        lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, DTYPE_CODE[dtype], 0, batch)
+        log(f"[tile256 batched] {dtype} {batch} x {M}x{N}x{K} {lbl}")
+        assert lbl.startswith("tile256x256") and want in lbl, lbl
+        if want == "splitk=":
+            assert "splitk=1 " not in lbl, lbl
+        check_full(p, gpu_result(handle, p))
+        e = synth.make_problem(dtype, M, N, K, batch=batch, seed=42, ab_dist="small_int",
+                               c_dist="small_int" if dtype != "i8" else "uniform_int",
+                               c_range=(-8, 8))
+        check_full(e, gpu_result(handle, e), exact=True)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
 def test_batched(handle, dtype):
     for (M, N, K, batch, pad) in [(64, 64, 64, 512, 0), (17, 40, 48, 5, 0), (64, 64, 256, 3, 8),
