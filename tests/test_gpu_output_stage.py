@@ -115,6 +115,29 @@ def test_storage_types_and_scaling(handle, dtype, c_type, d_type):
         log(f"[out] {dtype} C:{c_type} D:{d_type} {M}x{N}x{K}: max err/bound {r:.3g}")
 
 
+@pytest.mark.parametrize("c_type", FLOAT_TYPES)
+@pytest.mark.parametrize("d_type", FLOAT_TYPES)
+def test_tile256_every_storage_pair(handle, c_type, d_type):
+    """The 256x256 tile's own epilogue (no split) with every C / D storage pair and alpha,
+    beta != 1, on a shape with partial tiles on both edges, compared in full: random bf16
+    inputs against the bound, exact-integer fp16 inputs bit for bit."""
+    import dense_mixed_precision_02_amd as dmp
+    M, N, K = 4000, 4112, 256
+    p = synth.make_problem("bf16", M, N, K, b_col=True, seed=57)
+    lbl = dmp.plan_label(M, N, K, p.lda, p.ldb, p.ldc, DTYPE_CODE["bf16"], 2)
+    log(f"[out tile256] C:{c_type} D:{d_type} {lbl}")
+    assert lbl.startswith("tile256x256") and "splitk=1 " in lbl, lbl
+    Cst = store_c(c_type, p.C)
+    c_exact = oracle.decode_c(c_type, Cst)
+    D = run_ex(handle, p, 0.75, -1.25, c_type, d_type, Cst=Cst)
+    P, S = product(p)
+    check_tol(p, logical(p, host_d(d_type, D)), P, S, logical(p, c_exact), 0.75, -1.25, d_type,
+              f"tile256 C:{c_type} D:{d_type}")
+    e = synth.make_problem("f16", M, N, K, seed=58, ab_dist="small_int", c_dist="small_int",
+                           c_range=(-8, 8))
+    exact_check(handle, e, d_type, c_type)
+
+
 @pytest.mark.parametrize("d_type", FLOAT_TYPES)
 def test_beta_zero_reads_no_c(handle, d_type):
     """beta = 0 with a NULL C pointer on the tile, split-K and element-wise paths."""
